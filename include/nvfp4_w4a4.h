@@ -1,0 +1,206 @@
+/*
+ * nvfp4_w4a4.h - C ABI of the NVFP4 W4A4 prefill linear layer for MI355X
+ * (gfx950).
+ *
+ * The layer is the prefill path of Mix-Quant: weights and activations are
+ * both quantised to NVFP4 and multiplied in a W4A4 GEMM ("Mix-Quant：面向
+ * 智能体LLM的量化预填充与精确解码", paper.rainbus.top digest, sections
+ * 核心方法 and 方法步骤详情 step (4); "Mix-Quant: Quantized Prefilling,
+ * Precise Decoding for Agentic LLMs", r9-hu.github.io digest, section
+ * Method, item 1).
+ *
+ * NVFP4 encoding produced and consumed here (the format of the paper.rainbus
+ * digest, section 前置知识 "NVFP4 微缩放量化", and the formulas of its
+ * section 方法步骤详情 step (3)):
+ *
+ *   alpha   one float32 per tensor:  alpha = RNE_fp32(max|x| / 2688),
+ *           2688 = 6 * 448 (q_max of E2M1 times the largest E4M3 value).
+ *   scales  uint8 [rows][K/16], row-major: OCP E4M3FN byte of
+ *           sigma_b = RNE_E4M3(max_{i in b}|x_i| / (6 alpha)), saturating
+ *           at 448, for the 16 consecutive K-elements of block b.
+ *   codes   uint8 [rows][K/2], row-major: E2M1 codes (sign in bit 3) of
+ *           q_i = RNE_E2M1(x_i / (alpha sigma_b)), ties to the even code,
+ *           saturating at 6; element 2j in the low nibble of byte j.
+ *           A block with sigma_b = 0 (or alpha = 0) gets magnitude 0.
+ *   Dequantised value: xhat_i = alpha * sigma_b * q_i.
+ *
+ * Every division above is taken in exact real arithmetic (no float32
+ * evaluation-order effects): codes and scale bytes are a pure function of
+ * the BF16 inputs and alpha.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  BF16 data is
+ *    passed as raw 16-bit patterns.  The library never allocates, keeps no
+ *    state between calls and is safe to call from several host threads.
+ *  - Work is enqueued on `stream` and is asynchronous; device faults surface
+ *    at the caller's next synchronisation.
+ *  - Arguments are validated first; on any error nothing is launched and the
+ *    status code says why.  Inputs must be finite (no NaN/Inf).
+ *  - Sizes are element counts.  K must be a positive multiple of 16.
+ *  - Pointer alignment: BF16 inputs 16 bytes (and ld*2 a multiple of 16),
+ *    codes 8 bytes, float outputs 16 bytes, BF16 outputs 8 bytes (ld_y a
+ *    multiple of 4); scales and alpha have no extra requirement.
+ */
+#ifndef NVFP4_W4A4_H
+#define NVFP4_W4A4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,          /* a required pointer is NULL                */
+  NVFP4_ERR_SHAPE = 2,         /* a size/stride is negative, too large, or  */
+                               /* K % 16 != 0, or group offsets malformed   */
+  NVFP4_ERR_ALIGN = 3,         /* a pointer or leading dimension misaligned */
+  NVFP4_ERR_UNSUPPORTED = 4,   /* the current device is not gfx950          */
+  NVFP4_ERR_LAUNCH = 5,        /* a HIP launch reported an error            */
+  NVFP4_ERR_WORKSPACE = 6      /* workspace NULL or smaller than required   */
+} nvfp4_status_t;
+
+/* Human-readable text of a status code (static storage). */
+const char* nvfp4_status_string(nvfp4_status_t status);
+
+/* Bytes of device workspace the quantisers need (a fixed, small amount). */
+size_t nvfp4_workspace_bytes(void);
+
+/*
+ * nvfp4_quantize_act - quantise a BF16 activation tensor X [M][K] (row
+ * stride ld_x elements) to NVFP4 on the fly.
+ *
+ *   alpha_in   NULL: alpha is computed from X on the device (amax pass);
+ *              otherwise the float32 at *alpha_in (device, finite, >= 0) is
+ *              used for every row.
+ *   alpha_out  device float32 receiving the alpha used (may equal alpha_in).
+ *   codes      device [M][K/2];  scales  device [M][K/16].
+ *   workspace  device scratch of nvfp4_workspace_bytes() bytes; the call
+ *              uses it as it runs on `stream` (calls that overlap in time
+ *              need separate workspaces).
+ * Formulas: paper.rainbus digest, 方法步骤详情 step (3); r9-hu digest,
+ * Method item 1.  M = 0 is allowed (nothing is launched unless alpha is to be
+ * computed, in which case alpha_out receives 0).
+ */
+nvfp4_status_t nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K,
+                                  int64_t ld_x, const float* alpha_in,
+                                  float* alpha_out, uint8_t* codes,
+                                  uint8_t* scales, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_quantize_weights - quantise a BF16 weight matrix (done once,
+ * offline: paper.rainbus digest, 核心方法; same format as the activations)
+ * into the GEMM's operand layout, N rows of K elements.
+ *
+ * Element (n, k) of the source is w_bf16[n * stride_n + k * stride_k], so a
+ * row-major N x K matrix has (stride_n, stride_k) = (K, 1) and a row-major
+ * K x N matrix has (1, N).  alpha is always computed from the whole matrix
+ * (one alpha per weight tensor; a grouped layer quantises each expert with
+ * its own call).  Outputs as for nvfp4_quantize_act.
+ */
+nvfp4_status_t nvfp4_quantize_weights(const void* w_bf16, int64_t N, int64_t K,
+                                      int64_t stride_n, int64_t stride_k,
+                                      float* alpha_out, uint8_t* codes,
+                                      uint8_t* scales, void* workspace,
+                                      size_t workspace_bytes,
+                                      hipStream_t stream);
+
+/*
+ * w4a4_gemm - Y[M][N] = (alpha_a alpha_b) * sum_k (sigma q)_a[m][k] *
+ * (sigma q)_b[n][k], the NVFP4 W4A4 linear layer (paper.rainbus digest,
+ * 核心方法 "W4A4" and 方法步骤详情 step (4)).  Products of dequantised
+ * operands are exact; they are accumulated in float32.
+ *
+ *   a_codes/a_scales  activation operand, [M][K/2] and [M][K/16]
+ *   b_codes/b_scales  weight operand,     [N][K/2] and [N][K/16]
+ *   alpha_a, alpha_b  device float32 scalars
+ *   y_f32   nullable, float32 [M][ld_y];  y_bf16  nullable, BF16 [M][ld_y]
+ *           (at least one non-NULL; BF16 is the RNE rounding of the float32
+ *           value).  ld_y >= N.
+ * M, N >= 0 (0 launches nothing), K >= 16.
+ */
+nvfp4_status_t w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+                         const float* alpha_a, const uint8_t* b_codes,
+                         const uint8_t* b_scales, const float* alpha_b,
+                         int64_t M, int64_t N, int64_t K, float* y_f32,
+                         uint16_t* y_bf16, int64_t ld_y, hipStream_t stream);
+
+/*
+ * w4a4_gemm_grouped - the W4A4 GEMM of a mixture-of-experts layer: one
+ * launch over num_groups experts with ragged row counts.
+ *
+ *   group_offsets  device int64 [num_groups + 1], non-decreasing,
+ *                  group_offsets[0] = 0 and group_offsets[num_groups] = M:
+ *                  GEMM rows [off[g], off[g+1]) use expert g.
+ *   a_row_index    nullable device int32 [M]: GEMM row r reads operand-A row
+ *                  a_row_index[r] (each in [0, a_rows)); NULL means row r.
+ *                  This gathers routed tokens straight from the quantised
+ *                  activation, which is bit-identical to quantising after the
+ *                  gather because one alpha covers the tensor.
+ *   b_codes/b_scales  [num_groups][N][K/2] and [num_groups][N][K/16]
+ *   alpha_b           device float32 [num_groups]
+ * The offsets are read on the device (no host synchronisation); malformed
+ * offsets are out of contract.
+ */
+nvfp4_status_t w4a4_gemm_grouped(const uint8_t* a_codes,
+                                 const uint8_t* a_scales, const float* alpha_a,
+                                 int64_t a_rows, const int32_t* a_row_index,
+                                 const uint8_t* b_codes,
+                                 const uint8_t* b_scales, const float* alpha_b,
+                                 int64_t M, int64_t N, int64_t K,
+                                 int32_t num_groups,
+                                 const int64_t* group_offsets, float* y_f32,
+                                 uint16_t* y_bf16, int64_t ld_y,
+                                 hipStream_t stream);
+
+/*
+ * w4a4_gemm_fused_act - the same layer with the activation quantiser fused
+ * into the GEMM: each workgroup quantises its BF16 A tile under alpha_a while
+ * it loads it, so the NVFP4 activation never goes through HBM.  alpha_a is a
+ * device float32 (e.g. from nvfp4_tensor_alpha); the call first rebuilds the
+ * exact decision tables for it in `workspace` (nvfp4_workspace_bytes()).
+ * Results are identical to nvfp4_quantize_act(alpha_in = alpha_a) followed by
+ * w4a4_gemm.  x_bf16 is [M][ld_x]; other arguments as for w4a4_gemm.
+ */
+nvfp4_status_t w4a4_gemm_fused_act(const void* x_bf16, int64_t ld_x,
+                                   const float* alpha_a,
+                                   const uint8_t* b_codes,
+                                   const uint8_t* b_scales,
+                                   const float* alpha_b, int64_t M, int64_t N,
+                                   int64_t K, float* y_f32, uint16_t* y_bf16,
+                                   int64_t ld_y, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_tensor_alpha - only the amax pass: alpha_out = RNE_fp32(max|x|/2688)
+ * of a BF16 tensor [M][K] (ld_x), for callers that fuse the quantiser.
+ */
+nvfp4_status_t nvfp4_tensor_alpha(const void* x_bf16, int64_t M, int64_t K,
+                                  int64_t ld_x, float* alpha_out,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/*
+ * bf16_gemm_baseline - the BF16 comparison GEMM (the pages compare NVFP4
+ * prefill against BF16: paper.rainbus digest, 实验结果 (3), Figure 4):
+ * Y[M][N] = X[M][K] . W[N][K]^T with BF16 operands, float32 accumulation.
+ * num_groups >= 1; with num_groups > 1, W is [num_groups][N][K] and
+ * group_offsets (device int64 [num_groups+1]) splits the rows of X as in
+ * w4a4_gemm_grouped (pass NULL when num_groups == 1).  K % 16 == 0.
+ */
+nvfp4_status_t bf16_gemm_baseline(const void* x_bf16, const void* w_bf16,
+                                  int64_t M, int64_t N, int64_t K,
+                                  int32_t num_groups,
+                                  const int64_t* group_offsets, float* y_f32,
+                                  uint16_t* y_bf16, int64_t ld_y,
+                                  hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_W4A4_H */

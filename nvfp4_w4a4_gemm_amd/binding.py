@@ -1,0 +1,248 @@
+"""ctypes binding of libnvfp4_w4a4.so with the C ABI's names.
+
+Argument marshalling only: torch tensors in (device memory, current HIP
+stream), raw pointers and sizes to the library, status codes back as
+exceptions.  Every step of the layer runs in the library's HIP kernels; if
+the library is missing the binding raises instead of computing anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_w4a4.so")
+
+_c_void = ctypes.c_void_p
+_c_i64 = ctypes.c_int64
+_c_i32 = ctypes.c_int32
+_c_size = ctypes.c_size_t
+
+# name -> argument types (all return nvfp4_status_t, an int)
+_SIGNATURES = {
+    "nvfp4_quantize_act": [_c_void, _c_i64, _c_i64, _c_i64, _c_void, _c_void, _c_void,
+                           _c_void, _c_void, _c_size, _c_void],
+    "nvfp4_quantize_weights": [_c_void, _c_i64, _c_i64, _c_i64, _c_i64, _c_void, _c_void,
+                               _c_void, _c_void, _c_size, _c_void],
+    "nvfp4_tensor_alpha": [_c_void, _c_i64, _c_i64, _c_i64, _c_void, _c_void, _c_size,
+                           _c_void],
+    "w4a4_gemm": [_c_void, _c_void, _c_void, _c_void, _c_void, _c_void, _c_i64, _c_i64,
+                  _c_i64, _c_void, _c_void, _c_i64, _c_void],
+    "w4a4_gemm_grouped": [_c_void, _c_void, _c_void, _c_i64, _c_void, _c_void, _c_void,
+                          _c_void, _c_i64, _c_i64, _c_i64, _c_i32, _c_void, _c_void,
+                          _c_void, _c_i64, _c_void],
+    "w4a4_gemm_fused_act": [_c_void, _c_i64, _c_void, _c_void, _c_void, _c_void, _c_i64,
+                            _c_i64, _c_i64, _c_void, _c_void, _c_i64, _c_void, _c_size,
+                            _c_void],
+    "bf16_gemm_baseline": [_c_void, _c_void, _c_i64, _c_i64, _c_i64, _c_i32, _c_void,
+                           _c_void, _c_void, _c_i64, _c_void],
+}
+
+EXPORTS = sorted(list(_SIGNATURES) + ["nvfp4_status_string", "nvfp4_workspace_bytes"])
+
+STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_ALIGN",
+          4: "NVFP4_ERR_UNSUPPORTED", 5: "NVFP4_ERR_LAUNCH", 6: "NVFP4_ERR_WORKSPACE"}
+
+_lib = None
+
+
+class NvFP4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)} "
+                         f"({lib().nvfp4_status_string(status).decode()})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m nvfp4_w4a4_gemm_amd.build` (no fallback exists)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        handle.nvfp4_status_string.argtypes = [ctypes.c_int]
+        handle.nvfp4_status_string.restype = ctypes.c_char_p
+        handle.nvfp4_workspace_bytes.argtypes = []
+        handle.nvfp4_workspace_bytes.restype = ctypes.c_size_t
+        _lib = handle
+    return _lib
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise NvFP4Error(name, st)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace_bytes() -> int:
+    return int(lib().nvfp4_workspace_bytes())
+
+
+def new_workspace(device) -> torch.Tensor:
+    return torch.empty(workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class NVFP4Tensor:
+    """A quantised operand: alpha (float32 [1]), scales [rows, K/16], codes [rows, K/2]."""
+    alpha: torch.Tensor
+    scales: torch.Tensor
+    codes: torch.Tensor
+
+    @property
+    def rows(self) -> int:
+        return self.codes.shape[-2]
+
+    @property
+    def k(self) -> int:
+        return self.codes.shape[-1] * 2
+
+
+def _check_bf16_2d(x: torch.Tensor, name: str):
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise ValueError(f"{name} must be a 2-D bfloat16 CUDA tensor")
+    if x.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along K")
+
+
+def nvfp4_quantize_act(x: torch.Tensor, alpha_in: torch.Tensor | None = None,
+                       out: NVFP4Tensor | None = None,
+                       workspace: torch.Tensor | None = None) -> NVFP4Tensor:
+    """Quantise a BF16 activation [M, K] (alpha from the tensor unless given)."""
+    _check_bf16_2d(x, "x")
+    m, k = x.shape
+    dev = x.device
+    if out is None:
+        out = NVFP4Tensor(torch.empty(1, dtype=torch.float32, device=dev),
+                          torch.empty(m, k // 16, dtype=torch.uint8, device=dev),
+                          torch.empty(m, k // 2, dtype=torch.uint8, device=dev))
+    ws = workspace if workspace is not None else new_workspace(dev)
+    _call("nvfp4_quantize_act", _ptr(x), m, k, x.stride(0), _ptr(alpha_in), _ptr(out.alpha),
+          _ptr(out.codes), _ptr(out.scales), _ptr(ws), ws.numel(), _stream(dev))
+    return out
+
+
+def nvfp4_quantize_weights(w: torch.Tensor, layout: str = "nk",
+                           workspace: torch.Tensor | None = None) -> NVFP4Tensor:
+    """Quantise a BF16 weight: layout "nk" for [N, K], "kn" for [K, N]."""
+    if w.dtype != torch.bfloat16 or w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous 2-D bfloat16 tensor")
+    if layout == "nk":
+        n, k = w.shape
+        sn, sk = k, 1
+    elif layout == "kn":
+        k, n = w.shape
+        sn, sk = 1, n
+    else:
+        raise ValueError("layout must be 'nk' or 'kn'")
+    dev = w.device
+    out = NVFP4Tensor(torch.empty(1, dtype=torch.float32, device=dev),
+                      torch.empty(n, k // 16, dtype=torch.uint8, device=dev),
+                      torch.empty(n, k // 2, dtype=torch.uint8, device=dev))
+    ws = workspace if workspace is not None else new_workspace(dev)
+    _call("nvfp4_quantize_weights", _ptr(w), n, k, sn, sk, _ptr(out.alpha), _ptr(out.codes),
+          _ptr(out.scales), _ptr(ws), ws.numel(), _stream(dev))
+    return out
+
+
+def nvfp4_tensor_alpha(x: torch.Tensor, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    _check_bf16_2d(x, "x")
+    alpha = torch.empty(1, dtype=torch.float32, device=x.device)
+    ws = workspace if workspace is not None else new_workspace(x.device)
+    _call("nvfp4_tensor_alpha", _ptr(x), x.shape[0], x.shape[1], x.stride(0), _ptr(alpha),
+          _ptr(ws), ws.numel(), _stream(x.device))
+    return alpha
+
+
+def _outputs(m, n, dev, want_f32, want_bf16, y_f32, y_bf16):
+    if want_f32 and y_f32 is None:
+        y_f32 = torch.empty(m, n, dtype=torch.float32, device=dev)
+    if want_bf16 and y_bf16 is None:
+        y_bf16 = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    return y_f32, y_bf16
+
+
+def w4a4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, f32: bool = True, bf16: bool = True,
+              y_f32: torch.Tensor | None = None, y_bf16: torch.Tensor | None = None):
+    """Y = (alpha_a alpha_b) sum (sigma q)_a (sigma q)_b -> (y_f32, y_bf16)."""
+    m, k = a.rows, a.k
+    n = b.rows
+    if b.k != k:
+        raise ValueError("operands disagree on K")
+    y_f32, y_bf16 = _outputs(m, n, a.codes.device, f32, bf16, y_f32, y_bf16)
+    ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
+    _call("w4a4_gemm", _ptr(a.codes), _ptr(a.scales), _ptr(a.alpha), _ptr(b.codes),
+          _ptr(b.scales), _ptr(b.alpha), m, n, k, _ptr(y_f32), _ptr(y_bf16), ld,
+          _stream(a.codes.device))
+    return y_f32, y_bf16
+
+
+def w4a4_gemm_grouped(a: NVFP4Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor,
+                      b_alpha: torch.Tensor, group_offsets: torch.Tensor,
+                      a_row_index: torch.Tensor | None = None, m: int | None = None,
+                      f32: bool = True, bf16: bool = True):
+    """Grouped (MoE) GEMM: b_* are [G, N, K/2], [G, N, K/16], [G] tensors."""
+    g, n, kc = b_codes.shape
+    k = kc * 2
+    if m is None:
+        m = a_row_index.numel() if a_row_index is not None else a.rows
+    y_f32, y_bf16 = _outputs(m, n, a.codes.device, f32, bf16, None, None)
+    ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
+    _call("w4a4_gemm_grouped", _ptr(a.codes), _ptr(a.scales), _ptr(a.alpha), a.rows,
+          _ptr(a_row_index), _ptr(b_codes), _ptr(b_scales), _ptr(b_alpha), m, n, k, g,
+          _ptr(group_offsets), _ptr(y_f32), _ptr(y_bf16), ld, _stream(a.codes.device))
+    return y_f32, y_bf16
+
+
+def w4a4_gemm_fused_act(x: torch.Tensor, alpha_a: torch.Tensor, b: NVFP4Tensor,
+                        f32: bool = True, bf16: bool = True,
+                        workspace: torch.Tensor | None = None):
+    """Quantise-on-load GEMM: BF16 activation x [M, K] under alpha_a."""
+    _check_bf16_2d(x, "x")
+    m, k = x.shape
+    n = b.rows
+    y_f32, y_bf16 = _outputs(m, n, x.device, f32, bf16, None, None)
+    ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
+    ws = workspace if workspace is not None else new_workspace(x.device)
+    _call("w4a4_gemm_fused_act", _ptr(x), x.stride(0), _ptr(alpha_a), _ptr(b.codes),
+          _ptr(b.scales), _ptr(b.alpha), m, n, k, _ptr(y_f32), _ptr(y_bf16), ld, _ptr(ws),
+          ws.numel(), _stream(x.device))
+    return y_f32, y_bf16
+
+
+def bf16_gemm_baseline(x: torch.Tensor, w: torch.Tensor,
+                       group_offsets: torch.Tensor | None = None,
+                       f32: bool = True, bf16: bool = True):
+    """BF16 comparison GEMM: Y = X W^T (w [N, K] or [G, N, K] with offsets)."""
+    _check_bf16_2d(x, "x")
+    m, k = x.shape
+    g = 1 if w.dim() == 2 else w.shape[0]
+    n = w.shape[-2]
+    y_f32, y_bf16 = _outputs(m, n, x.device, f32, bf16, None, None)
+    ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
+    _call("bf16_gemm_baseline", _ptr(x), _ptr(w), m, n, k, g, _ptr(group_offsets),
+          _ptr(y_f32), _ptr(y_bf16), ld, _stream(x.device))
+    return y_f32, y_bf16
+
+
+def to_device_bf16(bits, device) -> torch.Tensor:
+    """uint16 BF16 bit patterns (numpy) -> bfloat16 tensor on device."""
+    import numpy as np
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)

@@ -1,0 +1,48 @@
+// Device-side helpers shared by the HIP kernels of the NVFP4 W4A4 layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Quotient and remainder by a fixed divisor with one multiply-high
+// (round-up method; exact for every n < 2^31 and d < 2^31).
+struct FastDiv {
+  uint32_t d;
+  uint32_t mul;
+  uint32_t shift;
+};
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
+  uint64_t t = ((uint64_t)__umulhi(n, f.mul) + n) >> f.shift;
+  return (uint32_t)t;
+}
+
+// Maximum of the BF16 magnitudes packed in a 32-bit word pair list.
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  uint32_t lo = max(a & 0xFFFFu, b & 0xFFFFu);
+  uint32_t hi = max(a >> 16, b >> 16);
+  return lo | (hi << 16);
+}
+
+// Round-to-nearest-even float32 -> BF16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+}  // namespace nvfp4

@@ -22,8 +22,9 @@ What it computes (plain numpy, float64 unless stated):
   plus one tensor-level scale) is the one described in the same digest,
   section 前置知识, "NVFP4 微缩放量化".
 
-* The W4A4 linear layer Y = Xhat . What^T, accumulated in float64 (the
-  products of dequantised operands), and the matching bound
+* The W4A4 linear layer Y = Xhat . What^T.  Every dequantised value is
+  alpha * T * 2**-10 with a small integer T, so the sum over K is taken
+  exactly in integers and rounded once; also the bound
   B = |Xhat| . |What|^T used for the tolerance of a float32 result.
 
 Readings where the pages are silent (each one is also listed in the design
@@ -240,15 +241,61 @@ def gemm_ref(a_hat: np.ndarray, w_hat: np.ndarray):
     return y, bound
 
 
+def integer_operand(q):
+    """(alpha, scales, codes) -> int64 T with xhat = alpha * T * 2**-10 exactly.
+
+    T = (2 q) * (sigma * 2**9): 2q is an integer in [-12, 12] and every E4M3
+    value is an integer multiple of 2**-9 (at most 448 * 512 = 229376), so
+    |T| < 2**22.
+    """
+    _, scales, packed = q
+    code = unpack_codes(packed)
+    two_q = np.array([0, 1, 2, 3, 4, 6, 8, 12], dtype=np.int64)[code & 7]
+    two_q = np.where(code & 8, -two_q, two_q)
+    sig512 = np.rint(e4m3_decode(scales) * 512.0).astype(np.int64)
+    return two_q * np.repeat(sig512, GROUP, axis=1)
+
+
+def exact_dot(ta: np.ndarray, tb: np.ndarray) -> np.ndarray:
+    """Exact int64 S = ta . tb^T for |entries| < 2**22 and K <= 2**16.
+
+    Each operand is split into signed 11-bit halves; every float64 product of
+    halves is an integer below 2**22 and every partial sum of K of them is an
+    integer below 2**38, so the four float64 matrix products are exact in
+    any summation order.  S < 2**60 fits int64.
+    """
+    if ta.shape[1] > 1 << 16:
+        raise ValueError("K too large for the exact split")
+
+    def halves(t):
+        mag = np.abs(t)
+        sgn = np.sign(t)
+        return (sgn * (mag >> 11)).astype(np.float64), (sgn * (mag & 2047)).astype(np.float64)
+
+    a1, a0 = halves(ta)
+    b1, b0 = halves(tb)
+    p11 = (a1 @ b1.T).astype(np.int64)
+    p10 = (a1 @ b0.T).astype(np.int64) + (a0 @ b1.T).astype(np.int64)
+    p00 = (a0 @ b0.T).astype(np.int64)
+    return (p11 << 22) + (p10 << 11) + p00
+
+
 def w4a4_reference(a_q, w_q):
     """Reference of the W4A4 layer from two quantised operands.
 
     a_q, w_q: (alpha, scales, codes) triples as returned by ``quantize``.
-    Returns (Y float64 [M, N], B float64 [M, N], Y rounded to BF16 bits).
+    Y = sum_k xhat_a xhat_w = alpha_a alpha_w 2**-20 sum_k T_a T_w, with the
+    integer sum taken exactly (``exact_dot``) and then rounded once to
+    float64 (relative error <= 2**-52).
+    Returns (Y float64 [M, N], B = |Ahat| . |What|^T float64, Y rounded to
+    BF16 bits).
     """
-    a_hat = dequantize(*a_q)
-    w_hat = dequantize(*w_q)
-    y, bound = gemm_ref(a_hat, w_hat)
+    ta, tw = integer_operand(a_q), integer_operand(w_q)
+    s = exact_dot(ta, tw)
+    babs = exact_dot(np.abs(ta), np.abs(tw))
+    scale = float(np.float64(np.float32(a_q[0])) * np.float64(np.float32(w_q[0])))  # exact
+    y = s.astype(np.float64) * scale * 2.0 ** -20
+    bound = babs.astype(np.float64) * abs(scale) * 2.0 ** -20
     return y, bound, f64_to_bf16_bits(y)
 
 

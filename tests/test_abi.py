@@ -1,0 +1,157 @@
+"""The C-ABI library: it loads, exports every function include/*.h declares,
+and rejects bad arguments before launching anything.
+
+These tests make no compute calls.  Calls with otherwise valid arguments run
+with NVFP4_FORCE_ARCH set to a non-gfx950 name, so the library stops at the
+device check (NVFP4_ERR_UNSUPPORTED) on any machine, GPU or not.
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "nvfp4_w4a4_gemm_amd", "libnvfp4_w4a4.so")
+
+OK, NULL, SHAPE, ALIGN, UNSUPPORTED, LAUNCH, WORKSPACE = range(7)
+
+needs_lib = pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+
+
+def header_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_header_declares_the_four_entry_points():
+    names = header_functions()
+    for n in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "w4a4_gemm", "bf16_gemm_baseline"):
+        assert n in names
+
+
+@needs_lib
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(LIB)
+    for n in header_functions():
+        assert hasattr(lib, n), n
+
+
+@needs_lib
+def test_binding_signatures_cover_the_header():
+    from nvfp4_w4a4_gemm_amd import binding
+    assert set(binding.EXPORTS) == header_functions()
+
+
+@pytest.fixture
+def lib(monkeypatch):
+    monkeypatch.setenv("NVFP4_FORCE_ARCH", "gfx942")
+    from nvfp4_w4a4_gemm_amd import binding
+    return binding.lib()
+
+
+FAKE = 0x10000          # 64 KiB-aligned fake device address (never dereferenced)
+WS = 1 << 16
+
+
+def p(off=0):
+    return ctypes.c_void_p(FAKE + off)
+
+
+@needs_lib
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.nvfp4_status_string(s)
+    assert lib.nvfp4_workspace_bytes() > 0
+
+
+@needs_lib
+def test_quantize_act_validation(lib):
+    f = lib.nvfp4_quantize_act
+    # x, M, K, ld, alpha_in, alpha_out, codes, scales, ws, ws_bytes, stream
+    assert f(p(), 4, 32, 32, None, p(), p(), p(), p(), WS, None) == UNSUPPORTED
+    assert f(p(), 4, 33, 33, None, p(), p(), p(), p(), WS, None) == SHAPE   # K % 16
+    assert f(p(), 4, 0, 32, None, p(), p(), p(), p(), WS, None) == SHAPE    # K = 0
+    assert f(p(), -1, 32, 32, None, p(), p(), p(), p(), WS, None) == SHAPE  # M < 0
+    assert f(p(), 4, 32, 16, None, p(), p(), p(), p(), WS, None) == SHAPE   # ld < K
+    assert f(None, 4, 32, 32, None, p(), p(), p(), p(), WS, None) == NULL
+    assert f(p(), 4, 32, 32, None, None, p(), p(), p(), WS, None) == NULL   # alpha_out
+    assert f(p(), 4, 32, 32, None, p(), None, p(), p(), WS, None) == NULL
+    assert f(p(2), 4, 32, 32, None, p(), p(), p(), p(), WS, None) == ALIGN  # x
+    assert f(p(), 4, 32, 36, None, p(), p(), p(), p(), WS, None) == ALIGN   # ld * 2
+    assert f(p(), 4, 32, 32, None, p(), p(4), p(), p(), WS, None) == ALIGN  # codes
+    assert f(p(), 4, 32, 32, None, p(), p(), p(), None, WS, None) == WORKSPACE
+    assert f(p(), 4, 32, 32, None, p(), p(), p(), p(), 64, None) == WORKSPACE
+
+
+@needs_lib
+def test_quantize_weights_validation(lib):
+    f = lib.nvfp4_quantize_weights
+    # w, N, K, stride_n, stride_k, alpha_out, codes, scales, ws, ws_bytes, stream
+    assert f(p(), 8, 32, 32, 1, p(), p(), p(), p(), WS, None) == UNSUPPORTED
+    assert f(p(), 8, 32, 1, 8, p(), p(), p(), p(), WS, None) == UNSUPPORTED   # K x N source
+    assert f(p(), 8, 32, 2, 2, p(), p(), p(), p(), WS, None) == SHAPE         # neither unit
+    assert f(p(), 8, 40, 40, 1, p(), p(), p(), p(), WS, None) == SHAPE
+
+
+@needs_lib
+def test_gemm_validation(lib):
+    f = lib.w4a4_gemm
+    # a_codes, a_scales, alpha_a, b_codes, b_scales, alpha_b, M, N, K, y32, y16, ld, stream
+    args = [p(), p(), p(), p(), p(), p(), 64, 64, 256, p(), p(), 64, None]
+    assert f(*args) == UNSUPPORTED
+    bad = list(args); bad[8] = 40
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[6] = -1
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[9] = None; bad[10] = None
+    assert f(*bad) == NULL
+    bad = list(args); bad[11] = 32                           # ld_y < N
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[0] = p(8)
+    assert f(*bad) == ALIGN
+    bad = list(args); bad[9] = p(4)
+    assert f(*bad) == ALIGN
+    bad = list(args); bad[2] = None
+    assert f(*bad) == NULL
+    zero = list(args); zero[6] = 0                            # M = 0: nothing to do
+    assert f(*zero) == OK
+
+
+@needs_lib
+def test_grouped_and_fused_and_bf16_validation(lib):
+    g = lib.w4a4_gemm_grouped
+    # a_codes, a_scales, alpha_a, a_rows, a_row_index, b_codes, b_scales, alpha_b,
+    # M, N, K, groups, offsets, y32, y16, ld, stream
+    args = [p(), p(), p(), 100, None, p(), p(), p(), 100, 64, 128, 4, p(), p(), None, 64, None]
+    assert g(*args) == UNSUPPORTED
+    bad = list(args); bad[12] = None
+    assert g(*bad) == NULL
+    bad = list(args); bad[11] = 0
+    assert g(*bad) == SHAPE
+    bad = list(args); bad[3] = 10                             # fewer A rows than M
+    assert g(*bad) == SHAPE
+    fu = lib.w4a4_gemm_fused_act
+    # x, ld_x, alpha_a, b_codes, b_scales, alpha_b, M, N, K, y32, y16, ld, ws, ws_bytes, st
+    fargs = [p(), 128, p(), p(), p(), p(), 32, 64, 128, p(), None, 64, p(), WS, None]
+    assert fu(*fargs) == UNSUPPORTED
+    bad = list(fargs); bad[12] = None
+    assert fu(*bad) == WORKSPACE
+    bad = list(fargs); bad[1] = 100
+    assert fu(*bad) == SHAPE
+    b = lib.bf16_gemm_baseline
+    # x, w, M, N, K, groups, offsets, y32, y16, ld, stream
+    bargs = [p(), p(), 32, 64, 128, 1, None, p(), None, 64, None]
+    assert b(*bargs) == UNSUPPORTED
+    bad = list(bargs); bad[5] = 2
+    assert b(*bad) == NULL
+    bad = list(bargs); bad[4] = 24
+    assert b(*bad) == SHAPE
+    bad = list(bargs); bad[1] = p(2)
+    assert b(*bad) == ALIGN

@@ -341,13 +341,43 @@ def check_gemm_bruteforce(seed=0):
                             for t in range(k))
                 babs = sum(abs(Fraction(float(ah[i, t])) * Fraction(float(wh[j, t])))
                            for t in range(k))
-                assert abs(Fraction(float(y[i, j])) - exact) <= babs * Fraction(1, 2 ** 48)
+                assert abs(Fraction(float(y[i, j])) - exact) <= abs(exact) * Fraction(1, 2 ** 51)
                 assert abs(Fraction(float(bound[i, j])) - babs) <= babs * Fraction(1, 2 ** 48)
     return True
 
 
 def test_gemm_bruteforce_tiny():
     check_gemm_bruteforce()
+
+
+def check_gemm_exact_cancellation():
+    """Dot products that are exactly zero or tiny must come out exactly."""
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((8, 64)).astype(np.float32)
+    x[:, 32:] = x[:, :32]                      # second half repeats the first
+    xb = bf16_bits_of(x)
+    w = np.ones((3, 64), dtype=np.float32)
+    w[0, 32:] = -1.0                           # exact cancellation
+    w[1, 32:] = -1.0
+    w[1, 0] = 2.0 ** -6                        # plus one tiny term
+    wb = bf16_bits_of(w)
+    qa, qw = orc.quantize(xb), orc.quantize(wb)
+    y, bound, _ = orc.w4a4_reference(qa, qw)
+    ah, wh = orc.dequantize(*qa), orc.dequantize(*qw)
+    assert np.all(y[:, 0] == 0.0)
+    for i in range(8):
+        exact = sum(Fraction(float(ah[i, t])) * Fraction(float(wh[1, t])) for t in range(64))
+        assert abs(Fraction(float(y[i, 1])) - exact) <= abs(exact) * Fraction(1, 2 ** 52)
+    return True
+
+
+def bf16_bits_of(x):
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_gemm_exact_cancellation():
+    check_gemm_exact_cancellation()
 
 
 def test_gemm_one_hot():
@@ -384,7 +414,7 @@ def pins_pass() -> bool:
     checks = [check_golden_blocks, check_golden_gemm,
               lambda: sweep_e2m1(SWEEP_ALPHAS[:2], range(40, 127, 29)),
               lambda: sweep_e4m3(SWEEP_ALPHAS[:2]),
-              check_error_bound, check_gemm_bruteforce]
+              check_error_bound, check_gemm_bruteforce, check_gemm_exact_cancellation]
     for c in checks:
         try:
             c()
@@ -435,9 +465,13 @@ MUTANTS = {
                            lambda s: orc.round_to_minifloat(s, 1, 0, np.inf)),
     "dequant_drops_alpha": ("dequantize",
                             lambda a, s, p, f=orc.dequantize: f(1.0, s, p)),
-    "gemm_drops_last_k": ("gemm_ref",
-                          lambda a, w: (a[:, :-1] @ w[:, :-1].T,
-                                        np.abs(a) @ np.abs(w).T)),
+    "gemm_drops_last_k": ("exact_dot",
+                          lambda a, b, f=orc.exact_dot: f(a[:, :-1], b[:, :-1])),
+    "gemm_low_half_dropped": ("exact_dot",
+                              lambda a, b, f=orc.exact_dot: f(a & ~2047, b & ~2047)),
+    "gemm_float64_blas": ("exact_dot",
+                          lambda a, b: np.rint(a.astype(np.float64) @ b.astype(np.float64).T
+                                               * (1 + 2.0 ** -30)).astype(np.int64)),
 }
 
 
