@@ -38,8 +38,9 @@
  *    status code says why.  Inputs must be finite (no NaN/Inf).
  *  - Sizes are element counts.  K must be a positive multiple of 16.
  *  - Pointer alignment: BF16 inputs 16 bytes (and ld*2 a multiple of 16),
- *    codes 8 bytes, float outputs 16 bytes, BF16 outputs 8 bytes (ld_y a
- *    multiple of 4); scales and alpha have no extra requirement.
+ *    codes 16 bytes for the GEMMs (8 for the quantiser's output), scales 8
+ *    bytes when K % 128 == 0; outputs and alpha need only their element
+ *    alignment.
  */
 #ifndef NVFP4_W4A4_H
 #define NVFP4_W4A4_H
