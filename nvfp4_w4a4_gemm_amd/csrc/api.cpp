@@ -179,6 +179,10 @@ static nvfp4_status_t gemm_common(const uint8_t* a_codes, const uint8_t* a_scale
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16)) return NVFP4_ERR_ALIGN;
   if (K % 128 == 0 && (!aligned(a_scales, 8) || !aligned(b_scales, 8))) return NVFP4_ERR_ALIGN;
   if (a_row_index == nullptr && a_rows < M) return NVFP4_ERR_SHAPE;
+  // the kernels address each operand with 32-bit byte offsets
+  constexpr int64_t kMaxBytes = (int64_t(1) << 32) - 1;
+  if ((a_row_index ? a_rows : M) * (K / 2) > kMaxBytes || N * (K / 2) > kMaxBytes)
+    return NVFP4_ERR_SHAPE;
   if ((st = check_device()) != NVFP4_OK) return st;
   nvfp4::W4A4Args a;
   a.a_codes = a_codes;

@@ -1,4 +1,5 @@
-// NVFP4 W4A4 GEMM for gfx950 (dense and grouped).
+// NVFP4 W4A4 GEMM for gfx950 (dense, grouped, and with the activation
+// quantiser fused into the operand load).
 //
 // Y[m][n] = alpha_a alpha_b sum_b sigma^a_{m,b} sigma^b_{n,b}
 //           sum_{k in b} q^a_{m,k} q^b_{n,k}
@@ -12,24 +13,30 @@
 // q * sigma, however, has at most 6 significant bits and lies in
 // [2^-10, 2688], so it is exact in float16.  Each wave therefore decodes its
 // FP4 fragments to float16 with the block scale folded in
-// (v_cvt_scalef32_pk_f16_fp4 for the codes, then one packed f16 multiply by
-// sigma * 2^-4, which keeps every nonzero value a normal float16) and feeds
-// v_mfma_f32_32x32x16_f16.  Products are exact and accumulate in float32; the
-// epilogue multiplies by alpha_a alpha_b 2^8.  (An FP8 operand with sigma
-// folded in would round 5- and 6-bit products.)
+// (v_cvt_scalef32_pk_f16_fp4 gives the codes times 16, one packed f16
+// multiply applies sigma * 2^-8; every nonzero product is a normal float16)
+// and feeds v_mfma_f32_32x32x16_f16.  Products are exact and accumulate in
+// float32; the epilogue multiplies by alpha_a alpha_b 2^8.  (An FP8 operand
+// with sigma folded in would round 5- and 6-bit products.)
 //
 // Tiling: a 256-thread workgroup computes a BM x BN tile as 2 x 2 waves of
-// (BM/2) x (BN/2).  Each K-stage covers 128 elements (8 NVFP4 blocks): the
-// FP4 codes (BM and BN rows of 64 bytes) and the E4M3 scales (8 bytes a row)
-// go global -> registers -> LDS, double-buffered with one barrier a stage.
-// A lane of a 32x32x16 MFMA fragment holds 8 consecutive K-elements of one
-// row; lanes 0-31 take K-elements [0, 64) of the stage and lanes 32-63 take
-// [64, 128), eight per MFMA step, so a lane reads 32 contiguous code bytes
-// and 4 scale bytes per fragment and stage.  A and B use the same K order,
-// which is all the contraction needs.
+// (BM/2) x (BN/2).  Each K-stage covers 128 elements (8 NVFP4 blocks).  The
+// FP4 codes (64 bytes a row) and E4M3 scales (8 bytes a row) of a stage go
+// straight from global memory to LDS with buffer_load ... lds (no staging
+// registers); a ring of kRing stages keeps loads kRing - 1 stages ahead with
+// one barrier a stage.  A lane of a 32x32x16 MFMA fragment holds 8
+// consecutive K-elements of one row; lanes 0-31 take K-elements [0, 64) of
+// the stage and lanes 32-63 take [64, 128), eight per MFMA step, so a lane
+// reads 32 code bytes (two 16-byte chunks) and 4 scale bytes per fragment and
+// stage.  A and B use the same K order, which is all the contraction needs.
+// LDS rows are not padded; the 16-byte chunk c of row r sits at position
+// c ^ ((r >> 1) & 3) so that eight consecutive rows read conflict-free.
 #include "device_common.h"
 #include "kernels.h"
 #include "quant_block.h"
+
+#include <cstdlib>
+#include <cstring>
 
 namespace nvfp4 {
 
@@ -37,27 +44,63 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBK = 128;                 // K-elements per stage
-constexpr int kCodePitch = 80;           // LDS bytes per row (64 + 16 pad)
-constexpr int kScalePitch = 12;          // LDS bytes per row (8 + 4 pad)
+constexpr int kCodeRow = 64;             // LDS bytes of codes per row and stage
+constexpr int kScaleRow = 8;             // LDS bytes of scales per row and stage
 
-// sigma (E4M3FN byte) -> float16 sigma * 2^-4, replicated in both halves.
-__device__ __forceinline__ half2_t scale_pair(uint32_t sb) {
-  uint32_t bits = (sb << 7) | (sb << 23);        // = sigma * 2^-8 (exact)
-  half2_t h = __builtin_bit_cast(half2_t, bits);
-  const half2_t sixteen = {(_Float16)16.0f, (_Float16)16.0f};
-  return h * sixteen;                            // exact power-of-two scaling
+// global -> LDS DMA of 16 bytes (codes) or 4 bytes (scales) per lane: lane l
+// writes lds + l * bytes; lds must be the same for the whole wave.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff,
+                                      int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff,
+                                     int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
 }
 
-// 8 FP4 codes (one 32-bit word) -> 8 float16 values q * sigma * 2^-4.
-__device__ __forceinline__ half8_t decode8(uint32_t w, half2_t s) {
-  half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
-  half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
-  half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
-  half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+
+// s_waitcnt immediate (gfx9 encoding): vector-memory count n, no expcnt
+// wait, LDS/scalar count 0.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// Byte offset of 16-byte chunk c of row r inside a code tile.
+__device__ __forceinline__ int chunk_off(int row, int c) {
+  return row * kCodeRow + ((c ^ swz(row)) << 4);
+}
+
+// sigma (E4M3FN byte) -> float16 sigma * 2^-8 in both halves: the byte's
+// exponent and mantissa fields land in the f16 fields (a subnormal E4M3 byte
+// becomes a subnormal f16), i.e. bits (sb << 7) | (sb << 23).
+__device__ __forceinline__ uint32_t scale_pair_bits(uint32_t sb) {
+  return sb * 0x00800080u;
+}
+
+// 8 FP4 codes (one 32-bit word) -> 8 float16 values q * sigma * 2^-4: the
+// conversion applies the power of two 16 (its scale operand's exponent), the
+// packed multiply the scale; both products are exact.
+__device__ __forceinline__ half8_t decode8(uint32_t w, uint32_t s_bits) {
+  const half2_t s = __builtin_bit_cast(half2_t, s_bits);
+  half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 16.0f, 0);
+  half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 16.0f, 1);
+  half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 16.0f, 2);
+  half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 16.0f, 3);
+  p0 = p0 * s;
+  p1 = p1 * s;
+  p2 = p2 * s;
+  p3 = p3 * s;
   half8_t r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer (stride 0); dword 3 selects the plain 32-bit data format
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
 }
 
 struct TileCoord {
@@ -66,9 +109,9 @@ struct TileCoord {
   int group;
 };
 
-// Maps the workgroup to (group, row tile, column tile).  Dense GEMMs have one
-// group.  Grouped GEMMs launch an upper bound of row tiles (ceil(M/BM) +
-// groups) and walk the device-side offsets; surplus workgroups return.
+// Maps the workgroup to (group, row tile).  Dense GEMMs have one group.
+// Grouped GEMMs launch an upper bound of row tiles (ceil(M/BM) + groups) and
+// walk the device-side offsets; surplus workgroups return.
 template <int BM>
 __device__ __forceinline__ bool tile_coord(int tile_m, const int64_t* offsets,
                                            int num_groups, int64_t M,
@@ -94,15 +137,22 @@ __device__ __forceinline__ bool tile_coord(int tile_m, const int64_t* offsets,
   return false;
 }
 
+// kKAligned: K % 128 == 0 (stages are whole; codes and scales go by DMA).
 // kFused: operand A arrives as BF16 and each workgroup quantises its tile
 // into LDS with the exact tables (quant_block.h) instead of loading codes.
-template <int BM, int BN, bool kKAligned, bool kFused>
-__global__ __launch_bounds__(kThreads, 1) void w4a4_gemm_kernel(W4A4Args p) {
+// kRing: LDS stages in the ring (loads run kRing - 1 stages ahead; with 3 or
+// more the next stage's fragments are read while this one computes, with 2 at
+// the top of each stage).  kOcc: waves per SIMD
+// the register budget is sized for.
+template <int BM, int BN, bool kKAligned, bool kFused, int kRing, int kOcc>
+__global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   constexpr int WM = BM / 2, WN = BN / 2;      // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;    // 32x32 fragments per wave
-  constexpr int kStageBytes = (BM + BN) * kCodePitch + (BM + BN) * kScalePitch;
+  constexpr int kCodesA = 0, kCodesB = BM * kCodeRow;
+  constexpr int kScalesA = (BM + BN) * kCodeRow, kScalesB = kScalesA + BM * kScaleRow;
+  constexpr int kStageBytes = (BM + BN) * (kCodeRow + kScaleRow);
   constexpr int kTableBytes = kFused ? kSigLutN + kCodeLutN : 16;
-  __shared__ __align__(16) uint8_t lds[2 * kStageBytes];
+  __shared__ __align__(16) uint8_t lds[kRing * kStageBytes];
   __shared__ __align__(16) uint8_t lds_tables[kTableBytes];
 
   TileCoord tc;
@@ -118,106 +168,125 @@ __global__ __launch_bounds__(kThreads, 1) void w4a4_gemm_kernel(W4A4Args p) {
   const uint8_t* b_codes = p.b_codes + (int64_t)tc.group * p.N * kc;
   const uint8_t* b_scales = p.b_scales + (int64_t)tc.group * p.N * ks;
 
-  // ---- global -> register loader ------------------------------------------
-  // codes: row r = i * 64 + tid / 4 (i = 0..BM/64-1), 16-byte chunk tid % 4
-  constexpr int kARowIters = BM / 64, kBRowIters = BN / 64;
+  auto a_src_row = [&](int r) __attribute__((always_inline)) {
+    int64_t g = tc.m0 + r;
+    g = g < tc.m_end ? g : tc.m_end - 1;       // past the tile: clamp (not stored)
+    if (!kFused && p.a_row_index) g = p.a_row_index[g];
+    return g;
+  };
+  auto b_src_row = [&](int r) __attribute__((always_inline)) {
+    int64_t g = tc.n0 + r;
+    return g < p.N ? g : p.N - 1;
+  };
+
+  // ---- loader: DMA (K % 128 == 0) ---------------------------------------
+  // Code tile of R rows: WG instruction g (of R/16) moves rows [16g, 16g+16):
+  // lane l -> row 16g + l/4, LDS chunk position l % 4, global chunk
+  // (l % 4) ^ swz(row).  Wave w issues instructions g = w, w + 4, ...
+  // Scale tile: WG instruction g (of R/32) moves rows [32g, 32g+32): lane l
+  // -> row 32g + l/2, dword l % 2.
+  constexpr int kACodeIns = BM / 64, kBCodeIns = BN / 64;      // per wave
+  constexpr int kAScaleIns = BM / 128, kBScaleIns = BN / 128;  // per wave
+  // DMA instructions a wave issues per stage
+  constexpr int kDmaPerStage =
+      kKAligned ? (kFused ? 0 : kACodeIns + kAScaleIns) + kBCodeIns + kBScaleIns : 0;
+  static_assert(BM % 128 == 0 && BN % 128 == 0, "tile sizes");
+  uint32_t a_cv[kACodeIns], b_cv[kBCodeIns], a_sv[kAScaleIns], b_sv[kBScaleIns];
+#pragma unroll
+  for (int i = 0; i < kACodeIns; ++i) {
+    const int row = (i * 4 + wave) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz(row);
+    a_cv[i] = kFused ? 0u : (uint32_t)(a_src_row(row) * kc + c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < kBCodeIns; ++i) {
+    const int row = (i * 4 + wave) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz(row);
+    b_cv[i] = (uint32_t)(b_src_row(row) * kc + c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < kAScaleIns; ++i) {
+    const int row = (i * 4 + wave) * 32 + (lane >> 1);
+    a_sv[i] = kFused ? 0u : (uint32_t)(a_src_row(row) * ks + (lane & 1) * 4);
+  }
+#pragma unroll
+  for (int i = 0; i < kBScaleIns; ++i) {
+    const int row = (i * 4 + wave) * 32 + (lane >> 1);
+    b_sv[i] = (uint32_t)(b_src_row(row) * ks + (lane & 1) * 4);
+  }
+  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.a_codes, 0xFFFFFFFFu);
+  const __amdgpu_buffer_rsrc_t rs_as = make_rsrc(p.a_scales, 0xFFFFFFFFu);
+  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(b_codes, (uint32_t)(p.N * kc));
+  const __amdgpu_buffer_rsrc_t rs_bs = make_rsrc(b_scales, (uint32_t)(p.N * ks));
+
+  // ---- loader: registers (K % 128 != 0) ----------------------------------
+  // 16-byte chunk tid % 4 of rows i * 64 + tid / 4, read in 8-byte pieces
+  // with a bound; scales of row tid byte by byte.
   const int ld_chunk = tid & 3;
-  const uint8_t* a_row_ptr[kARowIters];
-  const uint8_t* b_row_ptr[kBRowIters];
-#pragma unroll
-  for (int i = 0; i < kARowIters; ++i) {
-    int64_t r = tc.m0 + i * 64 + (tid >> 2);
-    r = r < tc.m_end ? r : tc.m_end - 1;
-    if (!kFused && p.a_row_index) r = p.a_row_index[r];
-    a_row_ptr[i] = kFused ? nullptr : p.a_codes + r * kc + ld_chunk * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < kBRowIters; ++i) {
-    int64_t r = tc.n0 + i * 64 + (tid >> 2);
-    r = r < p.N ? r : p.N - 1;
-    b_row_ptr[i] = b_codes + r * kc + ld_chunk * 16;
-  }
-  // scales: row tid of A (and of B), 8 bytes a stage
-  const uint8_t* a_scale_ptr = nullptr;
-  const uint8_t* b_scale_ptr = nullptr;
-  if (!kFused && tid < BM) {
-    int64_t r = tc.m0 + tid;
-    r = r < tc.m_end ? r : tc.m_end - 1;
-    if (p.a_row_index) r = p.a_row_index[r];
-    a_scale_ptr = p.a_scales + r * ks;
-  }
+
   // fused A: thread -> (row, run of blocks) of the stage's BM x 8 blocks
   constexpr int kQBlocks = BM / 32;                // blocks per thread
   const int q_row = tid % BM, q_blk0 = (tid / BM) * kQBlocks;
   const uint16_t* q_src = nullptr;
   BlockTables tables;
   if (kFused) {
-    int64_t r = tc.m0 + q_row;
-    r = r < tc.m_end ? r : tc.m_end - 1;
-    q_src = p.a_bf16 + r * p.ld_a;
+    q_src = p.a_bf16 + a_src_row(q_row) * p.ld_a;
     load_tables_to_lds(p.ws, lds_tables, lds_tables + kSigLutN, tid, kThreads);
     tables = tables_from(p.ws, lds_tables, lds_tables + kSigLutN);
     __syncthreads();
   }
-  if (tid < BN) {
-    int64_t r = tc.n0 + tid;
-    r = r < p.N ? r : p.N - 1;
-    b_scale_ptr = b_scales + r * ks;
-  }
 
-  u32x4 ra[kARowIters], rb[kBRowIters];
-  u32x2 rsa = {0u, 0u}, rsb = {0u, 0u};
-
-  auto load_stage = [&](int kt) __attribute__((always_inline)) {
-    const int64_t kbyte = (int64_t)kt * (kBK / 2);         // code byte offset
+  // Issues the loads of stage kt into ring slot buf (DMA, or registers then
+  // LDS stores for the unaligned and fused paths, which complete here).
+  auto fill_stage = [&](int buf, int kt) __attribute__((always_inline)) {
+    uint8_t* base = lds + buf * kStageBytes;
     if (kKAligned) {
+      const int kcode = kt * (kBK / 2), kscale = kt * 8;
+      if (!kFused) {
 #pragma unroll
-      for (int i = 0; i < kARowIters; ++i)
-        if (!kFused) ra[i] = *reinterpret_cast<const u32x4*>(a_row_ptr[i] + kbyte);
+        for (int i = 0; i < kACodeIns; ++i)
+          dma16(rs_a, base + kCodesA + (i * 4 + wave) * 1024, a_cv[i], kcode);
 #pragma unroll
-      for (int i = 0; i < kBRowIters; ++i)
-        rb[i] = *reinterpret_cast<const u32x4*>(b_row_ptr[i] + kbyte);
-      if (!kFused && tid < BM) rsa = *reinterpret_cast<const u32x2*>(a_scale_ptr + kt * 8);
-      if (tid < BN) rsb = *reinterpret_cast<const u32x2*>(b_scale_ptr + kt * 8);
+        for (int i = 0; i < kAScaleIns; ++i)
+          dma4(rs_as, base + kScalesA + (i * 4 + wave) * 256, a_sv[i], kscale);
+      }
+#pragma unroll
+      for (int i = 0; i < kBCodeIns; ++i)
+        dma16(rs_b, base + kCodesB + (i * 4 + wave) * 1024, b_cv[i], kcode);
+#pragma unroll
+      for (int i = 0; i < kBScaleIns; ++i)
+        dma4(rs_bs, base + kScalesB + (i * 4 + wave) * 256, b_sv[i], kscale);
     } else {
-      // K % 128 != 0: 8-byte pieces (16 elements = one block) with a bound
+      const int64_t kbyte = (int64_t)kt * (kBK / 2);
       const int64_t k0 = (int64_t)kt * kBK + ld_chunk * 32;
       const bool v0 = k0 < K, v1 = k0 + 16 < K;
+      if (!kFused) {
 #pragma unroll
-      for (int i = 0; i < kARowIters; ++i) {
-        if (kFused) break;
-        const u32x2* q = reinterpret_cast<const u32x2*>(a_row_ptr[i] + kbyte);
-        u32x2 x0 = v0 ? q[0] : u32x2{0u, 0u};
-        u32x2 x1 = v1 ? q[1] : u32x2{0u, 0u};
-        ra[i] = u32x4{x0.x, x0.y, x1.x, x1.y};
+        for (int i = 0; i < BM / 64; ++i) {
+          const int row = i * 64 + (tid >> 2);
+          const u32x2* q = reinterpret_cast<const u32x2*>(p.a_codes + a_src_row(row) * kc + ld_chunk * 16 + kbyte);
+          const u32x2 x0 = v0 ? q[0] : u32x2{0u, 0u};
+          const u32x2 x1 = v1 ? q[1] : u32x2{0u, 0u};
+          *reinterpret_cast<u32x4*>(base + kCodesA + chunk_off(row, ld_chunk)) = u32x4{x0.x, x0.y, x1.x, x1.y};
+        }
       }
 #pragma unroll
-      for (int i = 0; i < kBRowIters; ++i) {
-        const u32x2* q = reinterpret_cast<const u32x2*>(b_row_ptr[i] + kbyte);
-        u32x2 x0 = v0 ? q[0] : u32x2{0u, 0u};
-        u32x2 x1 = v1 ? q[1] : u32x2{0u, 0u};
-        rb[i] = u32x4{x0.x, x0.y, x1.x, x1.y};
+      for (int i = 0; i < BN / 64; ++i) {
+        const int row = i * 64 + (tid >> 2);
+        const u32x2* q = reinterpret_cast<const u32x2*>(b_codes + b_src_row(row) * kc + ld_chunk * 16 + kbyte);
+        const u32x2 x0 = v0 ? q[0] : u32x2{0u, 0u};
+        const u32x2 x1 = v1 ? q[1] : u32x2{0u, 0u};
+        *reinterpret_cast<u32x4*>(base + kCodesB + chunk_off(row, ld_chunk)) = u32x4{x0.x, x0.y, x1.x, x1.y};
       }
-      uint32_t sa[2] = {0, 0}, sb[2] = {0, 0};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int64_t blk = (int64_t)kt * 8 + j;
-        if (blk < ks) {
-          if (!kFused && tid < BM) sa[j >> 2] |= (uint32_t)a_scale_ptr[blk] << (8 * (j & 3));
-          if (tid < BN) sb[j >> 2] |= (uint32_t)b_scale_ptr[blk] << (8 * (j & 3));
-        }
+        if (!kFused && tid < BM)
+          base[kScalesA + tid * kScaleRow + j] = blk < ks ? p.a_scales[a_src_row(tid) * ks + blk] : 0;
+        if (tid < BN)
+          base[kScalesB + tid * kScaleRow + j] = blk < ks ? b_scales[b_src_row(tid) * ks + blk] : 0;
       }
-      rsa = u32x2{sa[0], sa[1]};
-      rsb = u32x2{sb[0], sb[1]};
     }
-  };
-
-  auto store_stage = [&](int buf, int kt) __attribute__((always_inline)) {
-    uint8_t* base = lds + buf * kStageBytes;
-    uint8_t* a_lds = base;
-    uint8_t* b_lds = base + BM * kCodePitch;
-    uint8_t* as_lds = base + (BM + BN) * kCodePitch;
-    uint8_t* bs_lds = as_lds + BM * kScalePitch;
     if (kFused) {
 #pragma unroll
       for (int j = 0; j < kQBlocks; ++j) {
@@ -230,26 +299,10 @@ __global__ __launch_bounds__(kThreads, 1) void w4a4_gemm_kernel(W4A4Args p) {
           const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
           quantize16(w, tables, o0, o1, sbyte);
         }
-        *reinterpret_cast<u32x2*>(a_lds + q_row * kCodePitch + blk * 8) = u32x2{o0, o1};
-        as_lds[q_row * kScalePitch + blk] = (uint8_t)sbyte;
+        *reinterpret_cast<u32x2*>(base + kCodesA + chunk_off(q_row, blk >> 1) + 8 * (blk & 1)) =
+            u32x2{o0, o1};
+        base[kScalesA + q_row * kScaleRow + blk] = (uint8_t)sbyte;
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kARowIters; ++i)
-        *reinterpret_cast<u32x4*>(a_lds + (i * 64 + (tid >> 2)) * kCodePitch + ld_chunk * 16) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < kBRowIters; ++i)
-      *reinterpret_cast<u32x4*>(b_lds + (i * 64 + (tid >> 2)) * kCodePitch + ld_chunk * 16) = rb[i];
-    if (!kFused && tid < BM) {
-      uint32_t* q = reinterpret_cast<uint32_t*>(as_lds + tid * kScalePitch);
-      q[0] = rsa.x;
-      q[1] = rsa.y;
-    }
-    if (tid < BN) {
-      uint32_t* q = reinterpret_cast<uint32_t*>(bs_lds + tid * kScalePitch);
-      q[0] = rsb.x;
-      q[1] = rsb.y;
     }
   };
 
@@ -264,63 +317,137 @@ __global__ __launch_bounds__(kThreads, 1) void w4a4_gemm_kernel(W4A4Args p) {
   const int nk = (int)((K + kBK - 1) / kBK);
   const int fr = lane & 31, fh = lane >> 5;
 
-  load_stage(0);
-  store_stage(0, 0);
-  __syncthreads();
+  // Raw fragments of one stage in two halves (code words of steps 0-3 and
+  // of steps 4-7), the scale bytes, and two sets of decoded operands: step
+  // s+1 is decoded while the MFMAs of step s issue.
+  // (the next stage's scale bytes go to asn/bsn: this stage's steps 4-7
+  // still decode with asc/bsc after the next stage's first half is read)
+  u32x4 ac0[TM], ac1[TM], bc0[TN], bc1[TN];
+  uint32_t asc[TM], bsc[TN], asn[TM], bsn[TN];
+  half8_t a_cur[TM], b_cur[TN], a_nxt[TM], b_nxt[TN];
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_stage(kt + 1);
-
+  auto read_half0 = [&](int buf) __attribute__((always_inline)) {
     const uint8_t* base = lds + buf * kStageBytes;
-    const uint8_t* a_lds = base;
-    const uint8_t* b_lds = base + BM * kCodePitch;
-    const uint8_t* as_lds = base + (BM + BN) * kCodePitch;
-    const uint8_t* bs_lds = as_lds + BM * kScalePitch;
-
-    u32x4 ac[TM][2], bc[TN][2];
-    uint32_t asc[TM], bsc[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int row = wm + i * 32 + fr;
-      const u32x4* q = reinterpret_cast<const u32x4*>(a_lds + row * kCodePitch + fh * 32);
-      ac[i][0] = q[0];
-      ac[i][1] = q[1];
-      asc[i] = *reinterpret_cast<const uint32_t*>(as_lds + row * kScalePitch + fh * 4);
+      ac0[i] = *reinterpret_cast<const u32x4*>(base + kCodesA + chunk_off(row, 2 * fh));
+      asn[i] = *reinterpret_cast<const uint32_t*>(base + kScalesA + row * kScaleRow + fh * 4);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int row = wn + j * 32 + fr;
-      const u32x4* q = reinterpret_cast<const u32x4*>(b_lds + row * kCodePitch + fh * 32);
-      bc[j][0] = q[0];
-      bc[j][1] = q[1];
-      bsc[j] = *reinterpret_cast<const uint32_t*>(bs_lds + row * kScalePitch + fh * 4);
+      bc0[j] = *reinterpret_cast<const u32x4*>(base + kCodesB + chunk_off(row, 2 * fh));
+      bsn[j] = *reinterpret_cast<const uint32_t*>(base + kScalesB + row * kScaleRow + fh * 4);
     }
-
+  };
+  auto take_scales = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      half8_t af[TM], bf[TN];
+    for (int i = 0; i < TM; ++i) asc[i] = asn[i];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const u32x4 c = ac[i][s >> 2];
-        const uint32_t w = (s & 3) == 0 ? c.x : (s & 3) == 1 ? c.y : (s & 3) == 2 ? c.z : c.w;
-        af[i] = decode8(w, scale_pair((asc[i] >> (8 * (s >> 1))) & 0xFF));
-      }
+    for (int j = 0; j < TN; ++j) bsc[j] = bsn[j];
+  };
+  auto read_half1 = [&](int buf) __attribute__((always_inline)) {
+    const uint8_t* base = lds + buf * kStageBytes;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const u32x4 c = bc[j][s >> 2];
-        const uint32_t w = (s & 3) == 0 ? c.x : (s & 3) == 1 ? c.y : (s & 3) == 2 ? c.z : c.w;
-        bf[j] = decode8(w, scale_pair((bsc[j] >> (8 * (s >> 1))) & 0xFF));
-      }
+    for (int i = 0; i < TM; ++i)
+      ac1[i] = *reinterpret_cast<const u32x4*>(base + kCodesA + chunk_off(wm + i * 32 + fr, 2 * fh + 1));
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < TN; ++j)
+      bc1[j] = *reinterpret_cast<const u32x4*>(base + kCodesB + chunk_off(wn + j * 32 + fr, 2 * fh + 1));
+  };
+  auto word = [](const u32x4 c, int s) __attribute__((always_inline)) {
+    return (s & 3) == 0 ? c.x : (s & 3) == 1 ? c.y : (s & 3) == 2 ? c.z : c.w;
+  };
+  auto decode_with = [&](int s, half8_t (&ad)[TM], half8_t (&bd)[TN], const uint32_t (&sa)[TM],
+                         const uint32_t (&sb)[TN]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < TM; ++i)
+      ad[i] = decode8(word(s < 4 ? ac0[i] : ac1[i], s),
+                      scale_pair_bits((sa[i] >> (8 * (s >> 1))) & 0xFF));
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bd[j] = decode8(word(s < 4 ? bc0[j] : bc1[j], s),
+                      scale_pair_bits((sb[j] >> (8 * (s >> 1))) & 0xFF));
+  };
+  auto decode_step = [&](int s, half8_t (&ad)[TM], half8_t (&bd)[TN]) __attribute__((always_inline)) {
+    decode_with(s, ad, bd, asc, bsc);
+  };
+  auto mfma_step = [&](const half8_t (&ad)[TM], const half8_t (&bd)[TN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ad[i], bd[j], acc[i][j], 0, 0, 0);
+  };
+  // one MFMA, then a quarter of the next step's decode, and so on
+  auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM * TN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  constexpr int kHalf0Reads = 2 * (TM + TN), kHalf1Reads = TM + TN;
 
-    if (kt + 1 < nk) store_stage(buf ^ 1, kt + 1);
-    __syncthreads();
+  // prologue: kRing - 1 stages in LDS
+#pragma unroll
+  for (int st = 0; st < kRing - 1; ++st)
+    if (st < nk) fill_stage(st, st);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (kRing >= 3) {
+    read_half0(0);
+    read_half1(0);
+    take_scales();
+    decode_step(0, a_cur, b_cur);
+  }
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ahead = kt + kRing - 1;           // the stage loaded this iteration
+    if (ahead < nk) fill_stage(ahead % kRing, ahead);
+    // the next stage's slot (read even on the last iteration, then unused)
+    const int nbuf = (kt + 1) % kRing;
+    if (kRing == 2) {
+      read_half0(kt & 1);
+      read_half1(kt & 1);
+      take_scales();
+      decode_step(0, a_cur, b_cur);
+    }
+    decode_step(1, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave();
+    decode_step(2, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);  interleave();
+    decode_step(3, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave();
+    if (kRing >= 3) read_half0(nbuf);       // next stage: words of steps 0-3, scales
+    __builtin_amdgcn_sched_group_barrier(0x100, kHalf0Reads, 0);
+    decode_step(4, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);  interleave();
+    decode_step(5, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave();
+    decode_step(6, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);  interleave();
+    // step 6 also reads the next stage's second half once step 7's words are
+    // decoded (consumed at the next stage's step 3)
+    decode_step(7, a_nxt, b_nxt);
+    mfma_step(a_cur, b_cur);
+#pragma unroll
+    for (int i = 0; i < TM * TN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    if (kRing >= 3) read_half1(nbuf);
+    __builtin_amdgcn_sched_group_barrier(0x100, kHalf1Reads, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 7: decode the next stage's step 0 (its first half and scales are
+    // in registers since step 3) under this stage's last MFMAs
+    if (kRing >= 3) decode_with(0, a_cur, b_cur, asn, bsn);
+    mfma_step(a_nxt, b_nxt);
+    interleave();
+    if (kRing >= 3) take_scales();
+    // The next iteration reads stage kt + 2, loaded kRing - 3 iterations ago:
+    // with a 4-deep ring this iteration's loads stay in flight.  All LDS reads
+    // of this wave are complete (lgkmcnt 0) before the barrier, so the slot
+    // overwritten next iteration is free.
+    if (kRing >= 4 && ahead < nk) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerStage));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
   }
 
   // ---- epilogue ------------------------------------------------------------
@@ -345,38 +472,48 @@ __global__ __launch_bounds__(kThreads, 1) void w4a4_gemm_kernel(W4A4Args p) {
   }
 }
 
-template <int BM, int BN, bool kFused>
+template <int BM, int BN, bool kFused, int kRing, int kOcc>
 hipError_t launch_tiles(const W4A4Args& a, hipStream_t stream) {
-  int tiles_m;
-  if (a.group_offsets == nullptr) {
-    tiles_m = (int)((a.M + BM - 1) / BM);
-  } else {
-    tiles_m = (int)((a.M + BM - 1) / BM) + a.num_groups;
-  }
+  int tiles_m = (int)((a.M + BM - 1) / BM);
+  if (a.group_offsets != nullptr) tiles_m += a.num_groups;
   const int tiles_n = (int)((a.N + BN - 1) / BN);
   dim3 grid(tiles_m, tiles_n);
   if (a.K % kBK == 0)
-    hipLaunchKernelGGL((w4a4_gemm_kernel<BM, BN, true, kFused>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((w4a4_gemm_kernel<BM, BN, true, kFused, kRing, kOcc>), grid,
+                       dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((w4a4_gemm_kernel<BM, BN, false, kFused>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((w4a4_gemm_kernel<BM, BN, false, kFused, kRing, kOcc>), grid,
+                       dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+// Tile choice: NVFP4_GEMM_TILE (256x256, 128x256, 128x128) overrides the
+// size-based default, for tuning.
+template <bool kFused>
+hipError_t launch_any(const W4A4Args& a, hipStream_t stream) {
+  if (a.M == 0 || a.N == 0) return hipSuccess;
+  const char* env = std::getenv("NVFP4_GEMM_TILE");
+  int choice;
+  if (env != nullptr && std::strcmp(env, "256x256") == 0) choice = 0;
+  else if (env != nullptr && std::strcmp(env, "128x256") == 0) choice = 1;
+  else if (env != nullptr && std::strcmp(env, "128x128") == 0) choice = 2;
+  else {
+    const int64_t t0 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+    choice = t0 >= 256 ? 0 : 2;
+  }
+  if (choice == 0) return launch_tiles<256, 256, kFused, kFused ? 3 : 4, 1>(a, stream);
+  if (choice == 1) return launch_tiles<128, 256, kFused, 3, 1>(a, stream);
+  return launch_tiles<128, 128, kFused, 3, 2>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_w4a4(const W4A4Args& a, hipStream_t stream) {
-  if (a.M == 0 || a.N == 0) return hipSuccess;
-  // 256 x 256 tiles when they fill the 256 CUs, else 128 x 128.
-  const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (big >= 256) return launch_tiles<256, 256, false>(a, stream);
-  return launch_tiles<128, 128, false>(a, stream);
+  return launch_any<false>(a, stream);
 }
 
 hipError_t launch_w4a4_fused(const W4A4Args& a, hipStream_t stream) {
-  if (a.M == 0 || a.N == 0) return hipSuccess;
-  const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (big >= 256) return launch_tiles<256, 256, true>(a, stream);
-  return launch_tiles<128, 128, true>(a, stream);
+  return launch_any<true>(a, stream);
 }
 
 }  // namespace nvfp4

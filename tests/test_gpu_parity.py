@@ -184,6 +184,29 @@ def test_w4a4_gemm_matches_oracle(m, n, k):
     assert_gemm_close(y32, y16, y, bound, y16_ref)
 
 
+def test_w4a4_gemm_subnormal_scales():
+    """Rows whose every block scale is a subnormal E4M3 value (an outlier in
+    row 0 sets alpha), in both operands; B of those rows is made of them."""
+    m, n, k = 96, 80, 512
+    rng = np.random.default_rng(77)
+    x = (rng.standard_normal((m, k)) * 0.01).astype(np.float32)
+    x[0, 5] = 1000.0
+    w = (rng.standard_normal((n, k)) * 0.0002).astype(np.float32)
+    w[3, 7] = 20.0
+    xb, wb = bf16_bits(x), bf16_bits(w)
+    ra, rw = orc.quantize(xb), orc.quantize(wb)
+    assert (orc.e4m3_decode(ra[1][1:]) < 2.0 ** -6).mean() > 0.9
+    assert (orc.e4m3_decode(rw[1][4:]) < 2.0 ** -6).mean() > 0.5
+    qa = nv.nvfp4_quantize_act(dev_bf16(xb))
+    qw = nv.nvfp4_quantize_weights(dev_bf16(wb))
+    assert_quant_equal(qa, ra)
+    y32, y16 = nv.w4a4_gemm(qa, qw)
+    y, bound, y16_ref = orc.w4a4_reference(ra, rw)
+    assert_gemm_close(y32, y16, y, bound, y16_ref)
+    f32, _ = nv.w4a4_gemm_fused_act(dev_bf16(xb), qa.alpha, qw)
+    assert torch.equal(y32, f32)
+
+
 def test_w4a4_gemm_large_tile_path():
     # 256 x 256 tiles are used when they give >= 256 workgroups
     m, n, k = 4096, 4096, 256
