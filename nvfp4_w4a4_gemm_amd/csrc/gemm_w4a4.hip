@@ -140,10 +140,9 @@ __device__ __forceinline__ bool tile_coord(int tile_m, const int64_t* offsets,
 // kKAligned: K % 128 == 0 (stages are whole; codes and scales go by DMA).
 // kFused: operand A arrives as BF16 and each workgroup quantises its tile
 // into LDS with the exact tables (quant_block.h) instead of loading codes.
-// kRing: LDS stages in the ring (loads run kRing - 1 stages ahead; with 3 or
-// more the next stage's fragments are read while this one computes, with 2 at
-// the top of each stage).  kOcc: waves per SIMD
-// the register budget is sized for.
+// kRing: LDS stages in the ring (3 or 4; loads run kRing - 1 stages ahead and
+// the next stage's fragments are read while this one computes).  kOcc: waves
+// per SIMD the register budget is sized for.
 template <int BM, int BN, bool kKAligned, bool kFused, int kRing, int kOcc>
 __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   constexpr int WM = BM / 2, WN = BN / 2;      // wave tile
@@ -191,6 +190,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   constexpr int kDmaPerStage =
       kKAligned ? (kFused ? 0 : kACodeIns + kAScaleIns) + kBCodeIns + kBScaleIns : 0;
   static_assert(BM % 128 == 0 && BN % 128 == 0, "tile sizes");
+  static_assert(kRing == 3 || kRing == 4, "ring depth");
   uint32_t a_cv[kACodeIns], b_cv[kBCodeIns], a_sv[kAScaleIns], b_sv[kBScaleIns];
 #pragma unroll
   for (int i = 0; i < kACodeIns; ++i) {
@@ -397,28 +397,32 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
     if (st < nk) fill_stage(st, st);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (kRing >= 3) {
-    read_half0(0);
-    read_half1(0);
-    take_scales();
-    decode_step(0, a_cur, b_cur);
-  }
+  read_half0(0);
+  read_half1(0);
+  take_scales();
+  decode_step(0, a_cur, b_cur);
 
   for (int kt = 0; kt < nk; ++kt) {
     const int ahead = kt + kRing - 1;           // the stage loaded this iteration
     if (ahead < nk) fill_stage(ahead % kRing, ahead);
     // the next stage's slot (read even on the last iteration, then unused)
     const int nbuf = (kt + 1) % kRing;
-    if (kRing == 2) {
-      read_half0(kt & 1);
-      read_half1(kt & 1);
-      take_scales();
-      decode_step(0, a_cur, b_cur);
-    }
     decode_step(1, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave();
     decode_step(2, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);  interleave();
     decode_step(3, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave();
-    if (kRing >= 3) read_half0(nbuf);       // next stage: words of steps 0-3, scales
+    // Stage kt + 1 must have landed (every wave's loads) before its
+    // fragments are read; the loads of stages kt + 2 .. kt + kRing - 1 stay in
+    // flight.  The barrier also ends every wave's reads of stage kt (all
+    // issued in the previous iteration and complete at lgkmcnt 0), so the
+    // next iteration may refill its slot.
+    {
+      const int in_flight = nk - kt - 2;      // stages loaded after kt + 1
+      if (kRing >= 4 && in_flight >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kDmaPerStage));
+      else if (in_flight >= 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerStage));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_barrier();
+    }
+    read_half0(nbuf);                       // next stage: words of steps 0-3, scales
     __builtin_amdgcn_sched_group_barrier(0x100, kHalf0Reads, 0);
     decode_step(4, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);  interleave();
     decode_step(5, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave();
@@ -432,22 +436,15 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
-    if (kRing >= 3) read_half1(nbuf);
+    read_half1(nbuf);
     __builtin_amdgcn_sched_group_barrier(0x100, kHalf1Reads, 0);
     __builtin_amdgcn_sched_barrier(0);
     // step 7: decode the next stage's step 0 (its first half and scales are
     // in registers since step 3) under this stage's last MFMAs
-    if (kRing >= 3) decode_with(0, a_cur, b_cur, asn, bsn);
+    decode_with(0, a_cur, b_cur, asn, bsn);
     mfma_step(a_nxt, b_nxt);
     interleave();
-    if (kRing >= 3) take_scales();
-    // The next iteration reads stage kt + 2, loaded kRing - 3 iterations ago:
-    // with a 4-deep ring this iteration's loads stay in flight.  All LDS reads
-    // of this wave are complete (lgkmcnt 0) before the barrier, so the slot
-    // overwritten next iteration is free.
-    if (kRing >= 4 && ahead < nk) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerStage));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __builtin_amdgcn_s_barrier();
+    take_scales();
   }
 
   // ---- epilogue ------------------------------------------------------------

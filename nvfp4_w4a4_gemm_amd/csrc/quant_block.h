@@ -32,6 +32,63 @@ __device__ __forceinline__ void scale_class(uint32_t sb, int& e, int& k) {
   }
 }
 
+// Magnitude bits (BF16 without the sign) of the 2n values packed in w[n]
+// (element 2i in the low half of w[i]); on the slow path (alpha's exponent
+// beyond +-100) the magnitudes are first multiplied by 2^shift.
+template <int n>
+__device__ __forceinline__ void magnitudes(const uint32_t* w, const BlockTables& t,
+                                           uint32_t* mag) {
+#pragma unroll
+  for (int i = 0; i < n; ++i) {
+    mag[2 * i] = w[i] & 0x7FFFu;
+    mag[2 * i + 1] = (w[i] >> 16) & 0x7FFFu;
+  }
+  if (t.slow) {
+#pragma unroll
+    for (int i = 0; i < 2 * n; ++i) {
+      float f = ldexpf(bf16_bits_to_f32(mag[i]), t.shift);
+      mag[i] = __float_as_uint(f) >> 16;    // inf -> 0x7F80: clamps high
+    }
+  }
+}
+
+// Where a block's codes are found in the code table: the row of the scale's
+// mantissa class [lo, hi] and the offset added to an element's bits.
+struct CodeRow {
+  int lo, hi, off;
+};
+
+// Scale byte of a block whose largest magnitude has bits amax.
+__device__ __forceinline__ uint32_t block_scale(uint32_t amax, const BlockTables& t,
+                                                CodeRow& row) {
+  const int sidx = min(max((int)amax + t.sig_off, 0), kSigLutN - 1);
+  const uint32_t sb = t.sig[sidx];
+  row.lo = row.hi = row.off = 0;            // sigma = 0: every index hits entry 0 (code 0)
+  if (sb != 0) {
+    int e, k;
+    scale_class(sb, e, k);
+    row.lo = k * kCodeLutRow;
+    row.hi = row.lo + kCodeLutRow - 1;
+    row.off = t.code_off + row.lo - 128 * e;
+  }
+  return sb;
+}
+
+// Codes of 8 consecutive elements (magnitudes mag[8], packed values w[4]):
+// element i in nibble i, sign bit in bit 3 of the nibble.
+__device__ __forceinline__ uint32_t codes8(const uint32_t* mag, const uint32_t* w,
+                                           const CodeRow& row, const BlockTables& t) {
+  uint32_t o = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = min(max((int)mag[i] + row.off, row.lo), row.hi);
+    uint32_t c = t.code[idx];
+    c |= (w[i >> 1] >> ((i & 1) ? 28 : 12)) & 8u;    // sign bit -> bit 3
+    o |= c << (4 * i);
+  }
+  return o;
+}
+
 // w[8]: the 16 BF16 values of the block, two per word (element 2i in the low
 // half of w[i]).  Produces the 8 code bytes (out0: elements 0-7, out1: 8-15,
 // element 2j in the low nibble of byte j) and the scale byte.
@@ -39,45 +96,14 @@ __device__ __forceinline__ void quantize16(const uint32_t w[8], const BlockTable
                                            uint32_t& out0, uint32_t& out1,
                                            uint32_t& scale_byte) {
   uint32_t mag[16];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    mag[2 * i] = w[i] & 0x7FFFu;
-    mag[2 * i + 1] = (w[i] >> 16) & 0x7FFFu;
-  }
-  if (t.slow) {                             // alpha's exponent beyond +-100
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float f = ldexpf(bf16_bits_to_f32(mag[i]), t.shift);
-      mag[i] = __float_as_uint(f) >> 16;    // inf -> 0x7F80: clamps high
-    }
-  }
+  magnitudes<8>(w, t, mag);
   uint32_t amax = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = max(amax, mag[i]);
-
-  const int sidx = min(max((int)amax + t.sig_off, 0), kSigLutN - 1);
-  const uint32_t sb = t.sig[sidx];
-
-  int lo = 0, hi = 0, off = 0;
-  if (sb != 0) {
-    int e, k;
-    scale_class(sb, e, k);
-    lo = k * kCodeLutRow;
-    hi = lo + kCodeLutRow - 1;
-    off = t.code_off + lo - 128 * e;
-  }
-  uint32_t o0 = 0, o1 = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int idx = min(max((int)mag[i] + off, lo), hi);
-    uint32_t c = t.code[idx];
-    c |= (w[i >> 1] >> ((i & 1) ? 28 : 12)) & 8u;    // sign bit -> bit 3
-    if (i < 8) o0 |= c << (4 * i);
-    else o1 |= c << (4 * (i - 8));
-  }
-  out0 = o0;
-  out1 = o1;
-  scale_byte = sb;
+  CodeRow row;
+  scale_byte = block_scale(amax, t, row);
+  out0 = codes8(mag, w, row, t);
+  out1 = codes8(mag + 8, w + 4, row, t);
 }
 
 // Copies the two tables from the workspace into LDS (all threads of the

@@ -11,9 +11,11 @@
 //
 // with every quotient taken exactly.  Three launches on the caller's stream:
 //
-//   amax     grid-stride max of the BF16 magnitude bits -> per-WG partials.
-//   prepare  one workgroup: alpha from the partials (IEEE float32 division),
-//            then two exact decision tables for this alpha, built in float64
+//   amax     grid-stride max of the BF16 magnitude bits -> per-WG partials
+//            (a flat walk over 16-byte chunks when the rows are contiguous).
+//   prepare  a few workgroups, one table entry per thread: each reduces the
+//            partials to alpha (IEEE float32 division) and builds its slice
+//            of two exact decision tables for this alpha, in float64
 //            (a float64 quotient of these short operands lands on the
 //            correct side of every rounding midpoint and hits a midpoint only
 //            when the exact quotient does):
@@ -93,6 +95,55 @@ __device__ __forceinline__ void block_coords(uint32_t b, uint32_t rows,
   }
 }
 
+__device__ __forceinline__ uint32_t chunk_amax_bits(u32x4 v) {
+  uint32_t m = pk_max_u16(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu);
+  m = pk_max_u16(m, v.z & 0x7FFF7FFFu);
+  return pk_max_u16(m, v.w & 0x7FFF7FFFu);
+}
+
+// Writes the workgroup's maximum of m to partials[blockIdx.x].
+__device__ __forceinline__ void store_partial(uint32_t m, uint32_t* __restrict__ partials) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) r = max(r, red[i]);
+    partials[blockIdx.x] = r;
+  }
+}
+
+// Dense tensors (rows back to back) are walked flat in 4 KiB segments of 256
+// 16-byte chunks, one segment per wave and iteration: lane l takes chunks
+// l, l + 64, l + 128 and l + 192, so each load instruction covers 1 KiB and
+// the wave's four loads one contiguous 4 KiB range (DRAM-page friendly).
+constexpr int kSegChunks = 256;
+
+// Max over n 16-byte chunks (n even).
+__global__ __launch_bounds__(kThreads) void amax_flat_kernel(
+    const u32x4* __restrict__ x, uint64_t n, uint32_t* __restrict__ partials) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t nwaves = (uint64_t)gridDim.x * (kThreads / 64);
+  uint32_t m = 0;
+  uint64_t seg = (uint64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  for (; seg * kSegChunks < n; seg += nwaves) {
+    const uint64_t c0 = seg * kSegChunks + lane;
+    if (c0 + 192 < n) {
+      const u32x4 v0 = x[c0], v1 = x[c0 + 64], v2 = x[c0 + 128], v3 = x[c0 + 192];
+      m = pk_max_u16(m, pk_max_u16(pk_max_u16(chunk_amax_bits(v0), chunk_amax_bits(v1)),
+                                   pk_max_u16(chunk_amax_bits(v2), chunk_amax_bits(v3))));
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (c0 + 64 * u < n) m = pk_max_u16(m, chunk_amax_bits(x[c0 + 64 * u]));
+    }
+  }
+  store_partial(max(m & 0xFFFFu, m >> 16), partials);
+}
+
 template <bool kContig>
 __global__ __launch_bounds__(kThreads) void amax_kernel(
     const uint16_t* __restrict__ x, uint32_t rows, uint32_t kb, FastDiv div,
@@ -108,18 +159,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(
     load_block<kContig>(x, row, cb, stride_row, stride_k, w);
     m = max(m, block_amax_bits(w));
   }
-  // wave reduction, then across the 4 waves
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  __shared__ uint32_t red[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = red[0];
-#pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) r = max(r, red[i]);
-    partials[blockIdx.x] = r;
-  }
+  store_partial(m, partials);
 }
 
 // E4M3FN byte of the round-to-nearest-even value of v >= 0, saturating.
@@ -143,6 +183,12 @@ __device__ uint32_t e2m1_rne_code(double s) {
   return (uint32_t)rint(0.5 * s) + 4;                 // 4, 6
 }
 
+constexpr int kPrepareGrid = (kSigLutN + kCodeLutN + kThreads - 1) / kThreads;
+
+// Thread j of the grid writes table entry j (sig_lut, then code_lut).
+// Workgroup 0 also writes alpha_out and the parameters.  Every workgroup
+// reads *alpha_in; alpha_out may be the same float, since the value written
+// is the value read.
 __global__ __launch_bounds__(kThreads) void prepare_kernel(
     const uint32_t* __restrict__ partials, int n_partials,
     const float* __restrict__ alpha_in, float* __restrict__ alpha_out,
@@ -164,7 +210,6 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(
     // correctly rounded float32 division (IEEE): alpha = RNE(amax / 2688)
     alpha = bf16_bits_to_f32(m) / 2688.0f;
   }
-  __syncthreads();   // every thread has read *alpha_in before it is rewritten
 
   QuantParams* P = reinterpret_cast<QuantParams*>(ws + kWsParams);
   uint8_t* sig_lut = ws + kWsSigLut;
@@ -178,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(
     s = 1 - e;                              // alpha * 2^s in [1, 2)
   }
   const bool slow = !zero && (s > 100 || s < -100);
-  if (threadIdx.x == 0) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
     *alpha_out = alpha;
     QuantParams p;
     p.alpha = alpha;
@@ -198,15 +243,67 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(
     *P = p;
   }
   const double a = zero ? 1.0 : ldexp((double)alpha, s);   // exact
-  for (int j = threadIdx.x; j < kSigLutN; j += kThreads) {
+  const int j = blockIdx.x * kThreads + threadIdx.x;
+  if (j < kSigLutN) {
     double v = (double)bf16_bits_to_f32(kSigLutBase + j) / (6.0 * a);
     sig_lut[j] = (uint8_t)e4m3_rne_byte(v);
-  }
-  for (int j = threadIdx.x; j < kCodeLutN; j += kThreads) {
-    int k = j / kCodeLutRow, i = j - k * kCodeLutRow;
+  } else if (j < kSigLutN + kCodeLutN) {
+    const int c = j - kSigLutN;
+    int k = c / kCodeLutRow, i = c - k * kCodeLutRow;
     double d = a * (1.0 + 0.125 * k);                     // exact
     double q = (double)bf16_bits_to_f32(kCodeLutBase + i) / d;
-    code_lut[j] = (uint8_t)e2m1_rne_code(q);
+    code_lut[c] = (uint8_t)e2m1_rne_code(q);
+  }
+}
+
+// Dense tensor, flat segments as in amax_flat_kernel.  A 16-byte chunk is
+// half a block: lanes 2c and 2c + 1 hold the two halves of one block and
+// exchange their maxima (DPP quad permutation [1,0,3,2]).  Each lane writes
+// the 4 code bytes of its chunk (chunk c -> codes word c), the even lane the
+// scale byte (block c / 2).  n is even, so a block's two chunks are both in
+// range or both out.
+__global__ __launch_bounds__(kThreads) void quantize_flat_kernel(
+    const u32x4* __restrict__ x, uint64_t n, const uint8_t* __restrict__ ws,
+    uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  __shared__ __align__(16) uint8_t lds_sig[kSigLutN];
+  __shared__ __align__(16) uint8_t lds_code[kCodeLutN];
+  const int lane = threadIdx.x & 63;
+  const uint64_t nwaves = (uint64_t)gridDim.x * (kThreads / 64);
+  auto load_seg = [&](uint64_t seg, u32x4 (&v)[4]) __attribute__((always_inline)) {
+    const uint64_t c0 = seg * kSegChunks + lane;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = c0 + 64 * u < n ? x[c0 + 64 * u] : u32x4{0u, 0u, 0u, 0u};
+  };
+  // the first segment's loads are in flight while the tables are copied
+  uint64_t seg = (uint64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  u32x4 v[4];
+  load_seg(seg, v);
+  load_tables_to_lds(ws, lds_sig, lds_code, threadIdx.x, kThreads);
+  const BlockTables t = tables_from(ws, lds_sig, lds_code);
+  __syncthreads();
+
+  while (seg * kSegChunks < n) {
+    const uint64_t c0 = seg * kSegChunks + lane;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      uint32_t mag[8];
+      magnitudes<4>(w, t, mag);
+      uint32_t amax = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = max(amax, mag[i]);
+      amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0xB1, 0xF, 0xF, false));
+      CodeRow row;
+      const uint32_t sb = block_scale(amax, t, row);
+      const uint32_t o = codes8(mag, w, row, t);
+      const uint64_t c = c0 + 64 * u;
+      if (c < n) {
+        codes[c] = o;
+        if ((lane & 1) == 0) scales[c >> 1] = (uint8_t)sb;
+      }
+    }
+    seg += nwaves;
+    load_seg(seg, v);
   }
 }
 
@@ -222,22 +319,36 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   __syncthreads();
 
   const uint32_t nb = rows * kb;
-  for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < nb;
-       b += gridDim.x * kThreads) {
-    int64_t row;
-    uint32_t cb;
-    block_coords<kContig>(b, rows, kb, div, row, cb);
-    uint32_t w[8];
-    load_block<kContig>(x, row, cb, stride_row, stride_k, w);
+  const uint32_t stride = gridDim.x * kThreads;
+  // codes are [rows][K/2]: block (row, cb) starts at byte 8 * (row kb + cb)
+  auto one = [&](uint32_t b, const uint32_t (&w)[8], int64_t row, uint32_t cb)
+      __attribute__((always_inline)) {
     uint32_t out0, out1, sb;
     quantize16(w, t, out0, out1, sb);
-    // codes are [rows][K/2]: block (row, cb) starts at byte 8 * (row kb + cb)
     const uint32_t ob = (uint32_t)row * kb + cb;
-    u32x2 o;
-    o.x = out0;
-    o.y = out1;
-    *reinterpret_cast<u32x2*>(codes + (size_t)ob * 8) = o;
+    *reinterpret_cast<u32x2*>(codes + (size_t)ob * 8) = u32x2{out0, out1};
     scales[ob] = (uint8_t)sb;
+  };
+  uint32_t b = blockIdx.x * kThreads + threadIdx.x;
+  // two blocks per lane and iteration: four 16-byte loads in flight
+  for (; b + stride < nb; b += 2 * stride) {
+    int64_t r0, r1;
+    uint32_t c0, c1;
+    block_coords<kContig>(b, rows, kb, div, r0, c0);
+    block_coords<kContig>(b + stride, rows, kb, div, r1, c1);
+    uint32_t w0[8], w1[8];
+    load_block<kContig>(x, r0, c0, stride_row, stride_k, w0);
+    load_block<kContig>(x, r1, c1, stride_row, stride_k, w1);
+    one(b, w0, r0, c0);
+    one(b + stride, w1, r1, c1);
+  }
+  if (b < nb) {
+    int64_t r0;
+    uint32_t c0;
+    block_coords<kContig>(b, rows, kb, div, r0, c0);
+    uint32_t w0[8];
+    load_block<kContig>(x, r0, c0, stride_row, stride_k, w0);
+    one(b, w0, r0, c0);
   }
 }
 
@@ -277,6 +388,16 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t k,
   if (grid > kAmaxPartials) grid = kAmaxPartials;
   *n_partials = grid;
   uint32_t* partials = reinterpret_cast<uint32_t*>(ws + kWsPartials);
+  if (contig && stride_row == k) {
+    const uint64_t n = (uint64_t)rows * (uint64_t)k / 8;      // 16-byte chunks
+    const int64_t segs = (int64_t)((n + kSegChunks - 1) / kSegChunks);
+    const int64_t need = (segs + 3) / 4;
+    grid = (int)(need < kAmaxPartials ? (need > 0 ? need : 1) : kAmaxPartials);
+    *n_partials = grid;
+    hipLaunchKernelGGL(amax_flat_kernel, dim3(grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const u32x4*>(x), n, partials);
+    return hipGetLastError();
+  }
   FastDiv div = to_dev(make_fast_div(contig ? kb : (uint32_t)rows));
   if (contig)
     hipLaunchKernelGGL(amax_kernel<true>, dim3(grid), dim3(kThreads), 0, stream,
@@ -290,7 +411,7 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t k,
 hipError_t launch_prepare(const uint8_t* ws_partials, int n_partials,
                           const float* alpha_in, float* alpha_out, uint8_t* ws,
                           hipStream_t stream) {
-  hipLaunchKernelGGL(prepare_kernel, dim3(1), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL(prepare_kernel, dim3(kPrepareGrid), dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint32_t*>(ws_partials), n_partials,
                      alpha_in, alpha_out, ws);
   return hipGetLastError();
@@ -304,6 +425,16 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k,
   const uint32_t nb = (uint32_t)rows * kb;
   if (nb == 0) return hipSuccess;
   const bool contig = (stride_k == 1);
+  if (contig && stride_row == k) {
+    const uint64_t n = (uint64_t)rows * (uint64_t)k / 8;      // 16-byte chunks
+    const int64_t segs = (int64_t)((n + kSegChunks - 1) / kSegChunks);
+    const int64_t need = (segs + 3) / 4;                      // one segment per wave
+    const int grid = (int)(need < 2048 ? need : 2048);
+    hipLaunchKernelGGL(quantize_flat_kernel, dim3(grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const u32x4*>(x), n, ws,
+                       reinterpret_cast<uint32_t*>(codes), scales);
+    return hipGetLastError();
+  }
   const int grid = grid_for(nb, 8);
   FastDiv div = to_dev(make_fast_div(contig ? kb : (uint32_t)rows));
   if (contig) {
