@@ -196,13 +196,14 @@ def w4a4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, f32: bool = True, bf16: bool = Tru
 def w4a4_gemm_grouped(a: NVFP4Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor,
                       b_alpha: torch.Tensor, group_offsets: torch.Tensor,
                       a_row_index: torch.Tensor | None = None, m: int | None = None,
-                      f32: bool = True, bf16: bool = True):
+                      f32: bool = True, bf16: bool = True,
+                      y_f32: torch.Tensor | None = None, y_bf16: torch.Tensor | None = None):
     """Grouped (MoE) GEMM: b_* are [G, N, K/2], [G, N, K/16], [G] tensors."""
     g, n, kc = b_codes.shape
     k = kc * 2
     if m is None:
         m = a_row_index.numel() if a_row_index is not None else a.rows
-    y_f32, y_bf16 = _outputs(m, n, a.codes.device, f32, bf16, None, None)
+    y_f32, y_bf16 = _outputs(m, n, a.codes.device, f32, bf16, y_f32, y_bf16)
     ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
     _call("w4a4_gemm_grouped", _ptr(a.codes), _ptr(a.scales), _ptr(a.alpha), a.rows,
           _ptr(a_row_index), _ptr(b_codes), _ptr(b_scales), _ptr(b_alpha), m, n, k, g,
@@ -212,12 +213,14 @@ def w4a4_gemm_grouped(a: NVFP4Tensor, b_codes: torch.Tensor, b_scales: torch.Ten
 
 def w4a4_gemm_fused_act(x: torch.Tensor, alpha_a: torch.Tensor, b: NVFP4Tensor,
                         f32: bool = True, bf16: bool = True,
-                        workspace: torch.Tensor | None = None):
+                        workspace: torch.Tensor | None = None,
+                        y_f32: torch.Tensor | None = None,
+                        y_bf16: torch.Tensor | None = None):
     """Quantise-on-load GEMM: BF16 activation x [M, K] under alpha_a."""
     _check_bf16_2d(x, "x")
     m, k = x.shape
     n = b.rows
-    y_f32, y_bf16 = _outputs(m, n, x.device, f32, bf16, None, None)
+    y_f32, y_bf16 = _outputs(m, n, x.device, f32, bf16, y_f32, y_bf16)
     ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
     ws = workspace if workspace is not None else new_workspace(x.device)
     _call("w4a4_gemm_fused_act", _ptr(x), x.stride(0), _ptr(alpha_a), _ptr(b.codes),

@@ -1,0 +1,178 @@
+"""Parity at the full sizes of the five layer configurations.
+
+Each configuration's tensors are drawn by ``workloads`` (the same bytes the
+benchmark uses) and pushed through the C ABI in the launch configuration the
+benchmark times (BF16 output; the float32 output is requested in a second
+launch of the same kernel).  The oracle cannot quantise or multiply the
+largest tensors whole in test time, so:
+
+* alpha of every tensor is compared exactly (the oracle takes the amax of
+  the full BF16 tensor);
+* codes and scale bytes are compared bit-exactly on sampled rows: the first
+  and last row, the row holding the tensor's largest magnitude, and seeded
+  random rows (all rows where the tensor is small);
+* GEMM outputs are compared on a sampled row x column grid: the oracle
+  quantises only those rows of each operand, with the full-tensor alpha.
+
+The grouped (MoE) configuration gathers the quantised token rows by the
+seeded routing and checks rows of several experts, and the dense stack of
+configuration 4 checks that the quantise-on-load GEMM is bit-identical to
+quantise-then-GEMM at full size.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import nvfp4_oracle as orc
+from nvfp4_w4a4_gemm_amd import binding as nv
+from nvfp4_w4a4_gemm_amd.workloads import workload
+
+from test_gpu_parity import assert_gemm_close, host_bits
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+ROWS = 192          # sampled rows per tensor (beyond first / last / amax row)
+GEMM_ROWS = 48      # sampled output rows per GEMM
+GEMM_COLS = 192     # sampled output columns per GEMM
+
+
+def sample(n, count, seed, must=()):
+    rng = np.random.default_rng(seed)
+    if n <= count + len(must):
+        return np.arange(n)
+    picks = set(int(i) for i in must) | {0, n - 1}
+    picks |= set(int(i) for i in rng.choice(n, count, replace=False))
+    return np.array(sorted(picks))
+
+
+def oracle_alpha(bits):
+    amax = np.array([int((bits & np.uint16(0x7FFF)).max())], dtype=np.uint16)
+    return orc.tensor_scale(orc.bf16_to_f64(amax))
+
+
+def amax_row(bits):
+    return int(np.argmax((bits & np.uint16(0x7FFF)).max(axis=1)))
+
+
+class Quantized:
+    """A tensor quantised on the GPU, with the oracle's view of sampled rows."""
+
+    def __init__(self, name, bits, weights, seed):
+        self.name = name
+        self.bits = bits
+        self.alpha = oracle_alpha(bits)
+        x = nv.to_device_bf16(bits, DEV)
+        self.q = nv.nvfp4_quantize_weights(x) if weights else nv.nvfp4_quantize_act(x)
+        self.dev = x
+        torch.cuda.synchronize()
+        self.rows = sample(bits.shape[0], ROWS, seed, must=(amax_row(bits),))
+
+    def check(self):
+        assert self.q.alpha.item() == float(self.alpha), (self.name, self.q.alpha.item(), self.alpha)
+        ref = orc.quantize(self.bits[self.rows], alpha=self.alpha)
+        rows_t = torch.from_numpy(self.rows).to(DEV)
+        s = self.q.scales.index_select(0, rows_t).cpu().numpy()
+        c = self.q.codes.index_select(0, rows_t).cpu().numpy()
+        bad = np.argwhere(s != ref[1])
+        assert bad.size == 0, f"{self.name}: scale bytes differ at {bad[:4].tolist()}"
+        bad = np.argwhere(c != ref[2])
+        assert bad.size == 0, f"{self.name}: code bytes differ at {bad[:4].tolist()}"
+
+    def oracle_rows(self, rows):
+        return orc.quantize(self.bits[rows], alpha=self.alpha)
+
+
+def check_gemm(name, a, w, seed, a_rows_of_output=None, out_rows=None):
+    """Full-size W4A4 GEMM on the GPU vs the oracle on a sampled grid."""
+    m = a.bits.shape[0] if a_rows_of_output is None else len(a_rows_of_output)
+    n = w.bits.shape[0]
+    y16 = torch.empty(m, n, dtype=torch.bfloat16, device=DEV)
+    nv.w4a4_gemm(a.q, w.q, f32=False, y_bf16=y16)
+    y32, _ = nv.w4a4_gemm(a.q, w.q, bf16=False)
+    torch.cuda.synchronize()
+    rows = out_rows if out_rows is not None else sample(m, GEMM_ROWS, seed)
+    cols = sample(n, GEMM_COLS, seed + 1)
+    src = rows if a_rows_of_output is None else a_rows_of_output[rows]
+    y, bound, y16_ref = orc.w4a4_reference(a.oracle_rows(src), w.oracle_rows(cols))
+    r_t, c_t = torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)
+    g32 = y32.index_select(0, r_t).index_select(1, c_t)
+    g16 = y16.index_select(0, r_t).index_select(1, c_t)
+    assert_gemm_close(g32, g16, y, bound, y16_ref)
+    print(f"[{name}] {m}x{n}x{a.bits.shape[1]}: {len(rows)}x{len(cols)} sampled outputs match")
+    return y16
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_dense_config(cfg):
+    wl = workload(cfg)
+    print(f"\n[cfg {cfg}] {wl.title}: generating", flush=True)
+    acts, wts = {}, {}
+    for i, g in enumerate(wl.gemms):
+        if g.act not in acts:
+            acts[g.act] = Quantized(g.act, wl.tensors[g.act].full(), False, 100 * cfg + i)
+            acts[g.act].check()
+            print(f"[cfg {cfg}] {g.act} {acts[g.act].bits.shape}: alpha and "
+                  f"{len(acts[g.act].rows)} rows of codes/scales bit-exact", flush=True)
+        wts[g.weight] = Quantized(g.weight, wl.tensors[g.weight].full(), True, 200 * cfg + i)
+        wts[g.weight].check()
+        y16 = check_gemm(f"cfg {cfg} {g.name}", acts[g.act], wts[g.weight], 300 * cfg + i)
+        if cfg == 4:
+            # quantise-on-load: bit-identical to quantise-then-GEMM at full size
+            _, f16 = nv.w4a4_gemm_fused_act(acts[g.act].dev, acts[g.act].q.alpha,
+                                            wts[g.weight].q, f32=False)
+            torch.cuda.synchronize()
+            assert torch.equal(f16.view(torch.int16), y16.view(torch.int16)), g.name
+            print(f"[cfg 4 {g.name}] fused quantise-on-load GEMM bit-identical", flush=True)
+        del wts[g.weight]
+        torch.cuda.empty_cache()
+
+
+def test_grouped_moe_config():
+    wl = workload(5)
+    e_count, topk = wl.experts, wl.topk
+    token_of_row, offsets = wl.routing()
+    print(f"\n[cfg 5] {wl.title}: generating", flush=True)
+    x = Quantized("X", wl.tensors["X"].full(), False, 501)
+    x.check()
+    h = Quantized("H", wl.tensors["H"].full(), False, 502)
+    h.check()
+    w_gu = [wl.tensors[f"W_gu[{e}]"].full() for e in range(e_count)]
+    w_dn = [wl.tensors[f"W_down[{e}]"].full() for e in range(e_count)]
+    off_t = torch.from_numpy(offsets).to(DEV)
+    tok_t = torch.from_numpy(token_of_row).to(DEV)
+    rng = np.random.default_rng(503)
+    experts = sorted(set(int(e) for e in rng.choice(e_count, 6, replace=False)) | {0, e_count - 1})
+
+    for name, act, wbits, gather in (("gate_up", x, w_gu, tok_t), ("down", h, w_dn, None)):
+        qws = [nv.nvfp4_quantize_weights(nv.to_device_bf16(b, DEV)) for b in wbits]
+        b_codes = torch.stack([q.codes for q in qws])
+        b_scales = torch.stack([q.scales for q in qws])
+        b_alpha = torch.cat([q.alpha for q in qws])
+        del qws
+        m = int(offsets[-1])
+        n = wbits[0].shape[0]
+        y16 = torch.empty(m, n, dtype=torch.bfloat16, device=DEV)
+        nv.w4a4_gemm_grouped(act.q, b_codes, b_scales, b_alpha, off_t, a_row_index=gather,
+                             f32=False, y_bf16=y16)
+        y32, _ = nv.w4a4_gemm_grouped(act.q, b_codes, b_scales, b_alpha, off_t,
+                                      a_row_index=gather, bf16=False)
+        torch.cuda.synchronize()
+        for e in experts:
+            lo, hi = int(offsets[e]), int(offsets[e + 1])
+            alpha_w = oracle_alpha(wbits[e])
+            assert b_alpha[e].item() == float(alpha_w), (name, e)
+            rows = lo + sample(hi - lo, 8, 510 + e)
+            cols = sample(n, 96, 520 + e)
+            src = token_of_row[rows] if gather is not None else rows
+            wq = orc.quantize(wbits[e][cols], alpha=alpha_w)
+            ref_codes = b_codes[e].index_select(0, torch.from_numpy(cols).to(DEV)).cpu().numpy()
+            assert np.array_equal(ref_codes, wq[2]), (name, e)
+            y, bound, y16_ref = orc.w4a4_reference(act.oracle_rows(src), wq)
+            r_t, c_t = torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)
+            assert_gemm_close(y32.index_select(0, r_t).index_select(1, c_t),
+                              y16.index_select(0, r_t).index_select(1, c_t), y, bound, y16_ref)
+        print(f"[cfg 5 {name}] {m}x{n}x{wbits[0].shape[1]} grouped over {e_count} experts: "
+              f"experts {experts} sampled, match", flush=True)
+        del b_codes, b_scales, y16, y32
+        torch.cuda.empty_cache()
