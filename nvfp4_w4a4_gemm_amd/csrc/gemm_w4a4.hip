@@ -37,6 +37,7 @@
 
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 namespace nvfp4 {
 
@@ -219,6 +220,31 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(b_codes, (uint32_t)(p.N * kc));
   const __amdgpu_buffer_rsrc_t rs_bs = make_rsrc(b_scales, (uint32_t)(p.N * ks));
 
+  // With a 4-deep ring the DMA of a stage is spread over the first six MFMA
+  // groups of an iteration (kDmaPer instructions each) instead of being
+  // issued in one burst, so a wave never stalls its MFMA issue on a full
+  // memory queue.  These loads are branch-free: past the last stage they
+  // reload stage nk - 1 into the slot being refilled, which no wave reads
+  // again (it is neither the stage being computed nor the next two).
+  constexpr bool kSpread = kKAligned && !kFused && kRing == 4;
+  constexpr int kDmaGroups = 6;
+  constexpr int kDmaPer = (kDmaPerStage + kDmaGroups - 1) / kDmaGroups;
+  constexpr int kDmaBeforeWait = 3 * kDmaPer < kDmaPerStage ? 3 * kDmaPer : kDmaPerStage;
+  auto dma_one = [&](uint8_t* base, int kcode, int kscale, int idx) __attribute__((always_inline)) {
+    if (idx < kACodeIns) {
+      dma16(rs_a, base + kCodesA + (idx * 4 + wave) * 1024, a_cv[idx], kcode);
+    } else if (idx < kACodeIns + kAScaleIns) {
+      const int i = idx - kACodeIns;
+      dma4(rs_as, base + kScalesA + (i * 4 + wave) * 256, a_sv[i], kscale);
+    } else if (idx < kACodeIns + kAScaleIns + kBCodeIns) {
+      const int i = idx - kACodeIns - kAScaleIns;
+      dma16(rs_b, base + kCodesB + (i * 4 + wave) * 1024, b_cv[i], kcode);
+    } else {
+      const int i = idx - kACodeIns - kAScaleIns - kBCodeIns;
+      dma4(rs_bs, base + kScalesB + (i * 4 + wave) * 256, b_sv[i], kscale);
+    }
+  };
+
   // ---- loader: registers (K % 128 != 0) ----------------------------------
   // 16-byte chunk tid % 4 of rows i * 64 + tid / 4, read in 8-byte pieces
   // with a bound; scales of row tid byte by byte.
@@ -240,7 +266,11 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   // LDS stores for the unaligned and fused paths, which complete here).
   auto fill_stage = [&](int buf, int kt) __attribute__((always_inline)) {
     uint8_t* base = lds + buf * kStageBytes;
-    if (kKAligned) {
+    if (kSpread) {
+#pragma unroll
+      for (int idx = 0; idx < kDmaPerStage; ++idx)
+        dma_one(base, kt * (kBK / 2), kt * 8, idx);
+    } else if (kKAligned) {
       const int kcode = kt * (kBK / 2), kscale = kt * 8;
       if (!kFused) {
 #pragma unroll
@@ -380,14 +410,28 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ad[i], bd[j], acc[i][j], 0, 0, 0);
   };
-  // one MFMA, then a quarter of the next step's decode, and so on
-  auto interleave = [&]() __attribute__((always_inline)) {
+  // one MFMA, then a quarter of the next step's decode, and so on; the
+  // group's share of the stage DMA goes after its first MFMAs
+  auto interleave = [&](int n_dma = 0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TM * TN; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < n_dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
+  };
+  // DMA group g (0..5) of the stage loaded during iteration kt
+  auto dma_group = [&](int kt, int g) __attribute__((always_inline)) {
+    if (!kSpread) return 0;
+    int ahead = kt + kRing - 1;
+    uint8_t* base = lds + (ahead % kRing) * kStageBytes;
+    ahead = ahead < nk ? ahead : nk - 1;
+    int n = 0;
+#pragma unroll
+    for (int idx = g * kDmaPer; idx < (g + 1) * kDmaPer && idx < kDmaPerStage; ++idx, ++n)
+      dma_one(base, ahead * (kBK / 2), ahead * 8, idx);
+    return n;
   };
   constexpr int kHalf0Reads = 2 * (TM + TN), kHalf1Reads = TM + TN;
 
@@ -404,29 +448,40 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
 
   for (int kt = 0; kt < nk; ++kt) {
     const int ahead = kt + kRing - 1;           // the stage loaded this iteration
-    if (ahead < nk) fill_stage(ahead % kRing, ahead);
+    if (!kSpread && ahead < nk) fill_stage(ahead % kRing, ahead);
     // the next stage's slot (read even on the last iteration, then unused)
     const int nbuf = (kt + 1) % kRing;
-    decode_step(1, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave();
-    decode_step(2, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);  interleave();
-    decode_step(3, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave();
+    int nd = dma_group(kt, 0);
+    decode_step(1, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave(nd);
+    nd = dma_group(kt, 1);
+    decode_step(2, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);  interleave(nd);
+    nd = dma_group(kt, 2);
+    decode_step(3, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave(nd);
     // Stage kt + 1 must have landed (every wave's loads) before its
     // fragments are read; the loads of stages kt + 2 .. kt + kRing - 1 stay in
     // flight.  The barrier also ends every wave's reads of stage kt (all
     // issued in the previous iteration and complete at lgkmcnt 0), so the
     // next iteration may refill its slot.
     {
-      const int in_flight = nk - kt - 2;      // stages loaded after kt + 1
-      if (kRing >= 4 && in_flight >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kDmaPerStage));
-      else if (in_flight >= 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerStage));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      if (kSpread) {
+        // after kt + 1's loads: all of kt + 2's and the first part of kt + 3's
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerStage + kDmaBeforeWait));
+      } else {
+        const int in_flight = nk - kt - 2;    // stages loaded after kt + 1
+        if (kRing >= 4 && in_flight >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kDmaPerStage));
+        else if (in_flight >= 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerStage));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      }
       __builtin_amdgcn_s_barrier();
     }
     read_half0(nbuf);                       // next stage: words of steps 0-3, scales
     __builtin_amdgcn_sched_group_barrier(0x100, kHalf0Reads, 0);
-    decode_step(4, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);  interleave();
-    decode_step(5, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave();
-    decode_step(6, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);  interleave();
+    nd = dma_group(kt, 3);
+    decode_step(4, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);  interleave(nd);
+    nd = dma_group(kt, 4);
+    decode_step(5, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave(nd);
+    nd = dma_group(kt, 5);
+    decode_step(6, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);  interleave(nd);
     // step 6 also reads the next stage's second half once step 7's words are
     // decoded (consumed at the next stage's step 3)
     decode_step(7, a_nxt, b_nxt);
@@ -448,25 +503,61 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   }
 
   // ---- epilogue ------------------------------------------------------------
+  // The accumulators leave through LDS, one 32-row band (i) of the wave's
+  // tile at a time: the lanes write their values in the MFMA layout, then
+  // each lane reads back 16 contiguous bytes of one output row and stores
+  // them with one vector store.  Each wave has a region of its own in the
+  // (now idle) ring; a wave's LDS operations complete in order, so the band
+  // needs no barrier between its writes and reads.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no DMA still writing the ring
+  __syncthreads();                         // every wave is done with the ring
   const float scale = (*p.alpha_a) * p.alpha_b[tc.group] * 256.0f;
   const int64_t row_lim = tc.m0 + BM < tc.m_end ? tc.m0 + BM : tc.m_end;
+  constexpr int kPitch32 = WN * 4 + 32, kPitch16 = WN * 2 + 16;   // padded rows
+  static_assert(4 * 32 * kPitch32 <= kRing * kStageBytes, "epilogue bands fit the ring");
+  uint8_t* band = lds + wave * 32 * kPitch32;
+
+  auto write_out = [&](auto* y, int vec, auto convert) __attribute__((always_inline)) {
+    using T = typename std::remove_pointer<decltype(y)>::type;
+    constexpr int kE = (int)sizeof(T), kPitch = kE == 4 ? kPitch32 : kPitch16;
+    constexpr int kPer = 16 / kE;                    // elements per 16-byte chunk
+    constexpr int kChunks = 32 * WN / kPer;          // chunks in a band
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int64_t col = tc.n0 + wn + j * 32 + fr;
-      if (col >= p.N) continue;
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = tc.m0 + wm + i * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
-        if (row < row_lim) {
-          const float v = acc[i][j][r] * scale;
-          if (p.y_f32) p.y_f32[row * p.ld_y + col] = v;
-          if (p.y_bf16) p.y_bf16[row * p.ld_y + col] = (uint16_t)f32_to_bf16_bits(v);
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + 4 * fh + (r & 3);
+          *reinterpret_cast<T*>(band + row * kPitch + (32 * j + fr) * kE) =
+              convert(acc[i][j][r] * scale);
+        }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < kChunks / 64; ++q) {
+        const int e = (q * 64 + lane) * kPer;
+        const int row = e / WN, col = e % WN;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(band + row * kPitch + col * kE);
+        const int64_t grow = tc.m0 + wm + 32 * i + row;
+        const int64_t gcol = tc.n0 + wn + col;
+        if (grow < row_lim) {
+          T* dst = y + grow * p.ld_y + gcol;
+          if (vec && gcol + kPer <= p.N) {
+            *reinterpret_cast<u32x4*>(dst) = v;
+          } else {
+            const T* t = reinterpret_cast<const T*>(&v);
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+              if (gcol + k < p.N) dst[k] = t[k];
+          }
         }
       }
+      __builtin_amdgcn_wave_barrier();
     }
-  }
+  };
+  if (p.y_f32) write_out(p.y_f32, p.vec_f32, [](float v) { return v; });
+  if (p.y_bf16)
+    write_out(p.y_bf16, p.vec_bf16, [](float v) { return (uint16_t)f32_to_bf16_bits(v); });
 }
 
 template <int BM, int BN, bool kFused, int kRing, int kOcc>
@@ -487,8 +578,11 @@ hipError_t launch_tiles(const W4A4Args& a, hipStream_t stream) {
 // Tile choice: NVFP4_GEMM_TILE (256x256, 128x256, 128x128) overrides the
 // size-based default, for tuning.
 template <bool kFused>
-hipError_t launch_any(const W4A4Args& a, hipStream_t stream) {
-  if (a.M == 0 || a.N == 0) return hipSuccess;
+hipError_t launch_any(const W4A4Args& args, hipStream_t stream) {
+  if (args.M == 0 || args.N == 0) return hipSuccess;
+  W4A4Args a = args;
+  a.vec_f32 = (reinterpret_cast<uintptr_t>(a.y_f32) % 16 == 0) && (a.ld_y * 4) % 16 == 0;
+  a.vec_bf16 = (reinterpret_cast<uintptr_t>(a.y_bf16) % 16 == 0) && (a.ld_y * 2) % 16 == 0;
   const char* env = std::getenv("NVFP4_GEMM_TILE");
   int choice;
   if (env != nullptr && std::strcmp(env, "256x256") == 0) choice = 0;

@@ -68,6 +68,8 @@ struct W4A4Args {
   const uint16_t* a_bf16;
   int64_t ld_a;
   const uint8_t* ws;              // prepared decision tables for alpha_a
+  // set by the launcher: the output rows may be written 16 bytes at a time
+  int32_t vec_f32, vec_bf16;
 };
 hipError_t launch_w4a4(const W4A4Args& args, hipStream_t stream);
 hipError_t launch_w4a4_fused(const W4A4Args& args, hipStream_t stream);
