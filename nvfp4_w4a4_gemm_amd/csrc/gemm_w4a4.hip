@@ -160,7 +160,8 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   tc.n0 = (int64_t)blockIdx.y * BN;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform: keep it (and the DMA LDS addresses) in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
   const int64_t K = p.K;
   const int64_t kc = K / 2, ks = K / 16;       // row pitch of codes / scales
