@@ -518,47 +518,73 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   static_assert(4 * 32 * kPitch32 <= kRing * kStageBytes, "epilogue bands fit the ring");
   uint8_t* band = lds + wave * 32 * kPitch32;
 
-  auto write_out = [&](auto* y, int vec, auto convert) __attribute__((always_inline)) {
+  // Writes band i into LDS: float32 values one by one, BF16 values rounded
+  // two at a time (rows R and R + 1 of a column) by the hardware's RNE
+  // conversion.
+  auto band_f32 = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * fh + (r & 3);
+        *reinterpret_cast<float*>(band + row * kPitch32 + (32 * j + fr) * 4) =
+            acc[i][j][r] * scale;
+      }
+  };
+  auto band_bf16 = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int row = 8 * (r >> 2) + 4 * fh + (r & 3);
+        const bf16x2_t h = __builtin_convertvector(
+            (float2_t){acc[i][j][r] * scale, acc[i][j][r + 1] * scale}, bf16x2_t);
+        __bf16* dst = reinterpret_cast<__bf16*>(band + row * kPitch16 + (32 * j + fr) * 2);
+        dst[0] = h[0];
+        dst[kPitch16 / 2] = h[1];
+      }
+  };
+  // Reads band i back in 16-byte row chunks and stores them.
+  auto band_store = [&](auto* y, int vec, int i) __attribute__((always_inline)) {
     using T = typename std::remove_pointer<decltype(y)>::type;
     constexpr int kE = (int)sizeof(T), kPitch = kE == 4 ? kPitch32 : kPitch16;
     constexpr int kPer = 16 / kE;                    // elements per 16-byte chunk
     constexpr int kChunks = 32 * WN / kPer;          // chunks in a band
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int q = 0; q < kChunks / 64; ++q) {
+      const int e = (q * 64 + lane) * kPer;
+      const int row = e / WN, col = e % WN;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(band + row * kPitch + col * kE);
+      const int64_t grow = tc.m0 + wm + 32 * i + row;
+      const int64_t gcol = tc.n0 + wn + col;
+      if (grow < row_lim) {
+        T* dst = y + grow * p.ld_y + gcol;
+        if (vec && gcol + kPer <= p.N) {
+          *reinterpret_cast<u32x4*>(dst) = v;
+        } else {
+          const T* t = reinterpret_cast<const T*>(&v);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 8 * (r >> 2) + 4 * fh + (r & 3);
-          *reinterpret_cast<T*>(band + row * kPitch + (32 * j + fr) * kE) =
-              convert(acc[i][j][r] * scale);
-        }
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int q = 0; q < kChunks / 64; ++q) {
-        const int e = (q * 64 + lane) * kPer;
-        const int row = e / WN, col = e % WN;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(band + row * kPitch + col * kE);
-        const int64_t grow = tc.m0 + wm + 32 * i + row;
-        const int64_t gcol = tc.n0 + wn + col;
-        if (grow < row_lim) {
-          T* dst = y + grow * p.ld_y + gcol;
-          if (vec && gcol + kPer <= p.N) {
-            *reinterpret_cast<u32x4*>(dst) = v;
-          } else {
-            const T* t = reinterpret_cast<const T*>(&v);
-#pragma unroll
-            for (int k = 0; k < kPer; ++k)
-              if (gcol + k < p.N) dst[k] = t[k];
-          }
+          for (int k = 0; k < kPer; ++k)
+            if (gcol + k < p.N) dst[k] = t[k];
         }
       }
-      __builtin_amdgcn_wave_barrier();
     }
   };
-  if (p.y_f32) write_out(p.y_f32, p.vec_f32, [](float v) { return v; });
-  if (p.y_bf16)
-    write_out(p.y_bf16, p.vec_bf16, [](float v) { return (uint16_t)f32_to_bf16_bits(v); });
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (p.y_f32) {
+      band_f32(i);
+      __builtin_amdgcn_wave_barrier();
+      band_store(p.y_f32, p.vec_f32, i);
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (p.y_bf16) {
+      band_bf16(i);
+      __builtin_amdgcn_wave_barrier();
+      band_store(reinterpret_cast<__bf16*>(p.y_bf16), p.vec_bf16, i);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
 }
 
 template <int BM, int BN, bool kFused, int kRing, int kOcc>
