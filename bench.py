@@ -54,8 +54,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rotate", type=int, default=4, help="input copies cycled over steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048,
+    ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="activation rows in the oracle's timed sample")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the layer step: time every GEMM and quantiser of the five "
+                         "layer configurations (one JSON line per configuration)")
+    ap.add_argument("--configs", default="1,2,3,4,5", help="configurations for --sweep")
     return ap.parse_args()
 
 
@@ -91,12 +95,30 @@ class Timer:
         self.pairs = {}
 
 
+def time_ms(torch, fn, reps, warmup):
+    """Mean milliseconds of fn(i) over reps calls (HIP events on the current stream)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(reps):
+        fn(warmup + i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this layer is measured on one GPU; multi-GPU sharding is "
                                    "described in DESIGN.md but not run", "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.sweep:
+        sweep(args)
+        return
 
     import numpy as np
     import torch
@@ -203,6 +225,21 @@ def main():
         f"({big_tflops:.0f} TFLOP/s); K/V GEMM {small_ms:.3f} ms; "
         f"quantize {quant_ms:.3f} ms ({quant_gbps:.0f} GB/s incl. amax)")
 
+    # --- quantiser passes on their own, and the attainable copy rate ----------
+    xq = [x["X_qkv"] for x in xs]
+    alpha_dev = qbuf["X_qkv"].alpha.clone()
+    n_el = m * h
+    t_alpha = time_ms(torch, lambda i: nv.nvfp4_tensor_alpha(xq[i % len(xq)], workspace=workspace),
+                      args.steps, args.warmup)
+    t_given = time_ms(torch, lambda i: nv.nvfp4_quantize_act(xq[i % len(xq)], alpha_in=alpha_dev,
+                                                             out=qbuf["X_qkv"],
+                                                             workspace=workspace),
+                      args.steps, args.warmup)
+    cpy = torch.empty_like(xq[0])
+    t_copy = time_ms(torch, lambda i: cpy.copy_(xq[i % len(xq)]), args.steps, args.warmup)
+    log(f"quantiser passes: amax+alpha {t_alpha * 1e3:.1f} us, quantize (alpha given) "
+        f"{t_given * 1e3:.1f} us; device copy of X {t_copy * 1e3:.1f} us")
+
     # --- comparisons ---------------------------------------------------------
     log("timing BF16 baseline step (same skeleton) and torch.matmul (hipBLASLt)")
     bf16_ms = time_steps(bf16_step, args.steps, args.warmup)
@@ -250,6 +287,9 @@ def main():
             "frac_of_hbm_peak": round(quant_gbps / HBM_PEAK_GBPS, 4),
             "ms_per_tensor": round(quant_ms, 4),
             "bytes_per_elem": QUANT_BYTES_PER_ELEM + AMAX_BYTES_PER_ELEM,
+            "amax_pass_gbps": round(n_el * AMAX_BYTES_PER_ELEM / (t_alpha * 1e-3) / 1e9, 1),
+            "quantize_pass_gbps": round(n_el * QUANT_BYTES_PER_ELEM / (t_given * 1e-3) / 1e9, 1),
+            "device_copy_gbps": round(2 * n_el * 2 / (t_copy * 1e-3) / 1e9, 1),
         },
         "gemm": {"ms_per_step": round(gemm_ms_step, 4),
                  "tflops": round(flops_step / (gemm_ms_step * 1e-3) / 1e12, 2),
@@ -264,6 +304,156 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x_host, w_host, args.cpu_rows, flops_step, m)
     print(json.dumps(result), flush=True)
+
+
+def sweep(args):
+    """Every GEMM and activation quantiser of configurations 1-5 on one GPU.
+
+    Per GEMM: the W4A4 kernel (BF16 out), the BF16 comparison kernel and
+    torch.matmul (hipBLASLt) on the same shapes; per activation tensor: the
+    whole quantiser (amax, alpha, tables, quantize).  Inputs rotate over
+    copies totalling at least 512 MB where a tensor is smaller, so reads come
+    from HBM.  Configuration 4 also times the quantise-on-load GEMM;
+    configuration 5 the grouped GEMMs (hipBLASLt as one matmul per expert).
+    """
+    import numpy as np
+    import torch
+
+    from nvfp4_w4a4_gemm_amd import binding as nv
+    from nvfp4_w4a4_gemm_amd.workloads import workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ws = nv.new_workspace(dev)
+    reps, warm = max(5, args.steps // 2), max(2, args.warmup)
+
+    def copies(bits):
+        n = max(1, min(8, -(-(512 << 20) // bits.nbytes)))
+        return [nv.to_device_bf16(np.roll(bits, r, axis=0) if r else bits, dev) for r in range(n)]
+
+    for cfg in [int(c) for c in args.configs.split(",")]:
+        wl = workload(cfg)
+        log(f"sweep: configuration {cfg}: {wl.title}")
+        out = {"config": cfg, "workload": wl.title, "gemms": [], "quantize": []}
+        if cfg == 5:
+            out.update(sweep_grouped(wl, nv, torch, dev, ws, copies, reps, warm))
+            print(json.dumps(out), flush=True)
+            continue
+        acts, qacts = {}, {}
+        for g in wl.gemms:
+            if g.act in acts:
+                continue
+            xs = copies(wl.tensors[g.act].full())
+            acts[g.act] = xs
+            q = nv.nvfp4_quantize_act(xs[0], workspace=ws)
+            qacts[g.act] = q
+            t = time_ms(torch, lambda i: nv.nvfp4_quantize_act(xs[i % len(xs)], out=q,
+                                                               workspace=ws), reps, warm)
+            el = xs[0].numel()
+            gbps = el * (QUANT_BYTES_PER_ELEM + AMAX_BYTES_PER_ELEM) / (t * 1e-3) / 1e9
+            out["quantize"].append({"tensor": g.act, "shape": list(xs[0].shape),
+                                    "ms": round(t, 4), "gbps": round(gbps, 1),
+                                    "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)})
+        layer = {"w4a4_ms": sum(q["ms"] for q in out["quantize"]), "bf16_ms": 0.0,
+                 "hipblaslt_ms": 0.0}
+        for g in wl.gemms:
+            w = nv.to_device_bf16(wl.tensors[g.weight].full(), dev)
+            qw = nv.nvfp4_quantize_weights(w, workspace=ws)
+            xs, qa = acts[g.act], qacts[g.act]
+            mm, kk, nn = xs[0].shape[0], xs[0].shape[1], w.shape[0]
+            y = torch.empty(mm, nn, dtype=torch.bfloat16, device=dev)
+            fl = 2.0 * mm * nn * kk
+            t4 = time_ms(torch, lambda i: nv.w4a4_gemm(qa, qw, f32=False, y_bf16=y), reps, warm)
+            tb = time_ms(torch, lambda i: nv.bf16_gemm_baseline(xs[i % len(xs)], w, f32=False),
+                         reps, warm)
+            th = time_ms(torch, lambda i: torch.matmul(xs[i % len(xs)], w.t()), reps, warm)
+            rec = {"gemm": g.name, "m": mm, "n": nn, "k": kk, "w4a4_ms": round(t4, 4),
+                   "tflops": round(fl / (t4 * 1e-3) / 1e12, 1),
+                   "frac_of_f16_mfma_peak": round(fl / (t4 * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                   "bf16_ms": round(tb, 4), "hipblaslt_ms": round(th, 4),
+                   "speedup_vs_bf16": round(tb / t4, 3), "speedup_vs_hipblaslt": round(th / t4, 3)}
+            if cfg == 4:
+                tf = time_ms(torch, lambda i: nv.w4a4_gemm_fused_act(
+                    xs[i % len(xs)], qa.alpha, qw, f32=False, y_bf16=y, workspace=ws), reps, warm)
+                rec["fused_quantize_gemm_ms"] = round(tf, 4)
+            out["gemms"].append(rec)
+            layer["w4a4_ms"] += t4
+            layer["bf16_ms"] += tb
+            layer["hipblaslt_ms"] += th
+            log(f"  {g.name} {mm}x{nn}x{kk}: w4a4 {t4:.3f} ms ({rec['tflops']} TFLOP/s), "
+                f"bf16 {tb:.3f} ms, hipBLASLt {th:.3f} ms")
+            del w, qw, y
+            torch.cuda.empty_cache()
+        layer["speedup_vs_bf16"] = round(layer["bf16_ms"] / layer["w4a4_ms"], 3)
+        layer["speedup_vs_hipblaslt"] = round(layer["hipblaslt_ms"] / layer["w4a4_ms"], 3)
+        out["layer"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in layer.items()}
+        print(json.dumps(out), flush=True)
+        del acts, qacts
+        torch.cuda.empty_cache()
+
+
+def sweep_grouped(wl, nv, torch, dev, ws, copies, reps, warm):
+    """Configuration 5: quantise X once, gather by routing, grouped GEMMs."""
+    token_of_row, offsets = wl.routing()
+    off_t = torch.from_numpy(offsets).to(dev)
+    tok_t = torch.from_numpy(token_of_row).to(dev)
+    res = {"gemms": [], "quantize": []}
+    xs = copies(wl.tensors["X"].full())
+    hs = copies(wl.tensors["H"].full())
+    layer = {"w4a4_ms": 0.0, "bf16_ms": 0.0, "hipblaslt_ms": 0.0}
+    for name, act, wname, gather in (("gate_up_proj", xs, "W_gu", tok_t),
+                                     ("down_proj", hs, "W_down", None)):
+        q = nv.nvfp4_quantize_act(act[0], workspace=ws)
+        t = time_ms(torch, lambda i: nv.nvfp4_quantize_act(act[i % len(act)], out=q, workspace=ws),
+                    reps, warm)
+        el = act[0].numel()
+        gbps = el * (QUANT_BYTES_PER_ELEM + AMAX_BYTES_PER_ELEM) / (t * 1e-3) / 1e9
+        res["quantize"].append({"tensor": "X" if gather is not None else "H",
+                                "shape": list(act[0].shape), "ms": round(t, 4),
+                                "gbps": round(gbps, 1),
+                                "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)})
+        layer["w4a4_ms"] += t
+        wbits = [wl.tensors[f"{wname}[{e}]"].full() for e in range(wl.experts)]
+        w = torch.stack([nv.to_device_bf16(b, dev) for b in wbits])
+        qws = [nv.nvfp4_quantize_weights(w[e], workspace=ws) for e in range(wl.experts)]
+        b_codes = torch.stack([qq.codes for qq in qws])
+        b_scales = torch.stack([qq.scales for qq in qws])
+        b_alpha = torch.cat([qq.alpha for qq in qws])
+        mm = int(offsets[-1])
+        nn, kk = w.shape[1], w.shape[2]
+        y = torch.empty(mm, nn, dtype=torch.bfloat16, device=dev)
+        fl = 2.0 * mm * nn * kk
+        t4 = time_ms(torch, lambda i: nv.w4a4_gemm_grouped(q, b_codes, b_scales, b_alpha, off_t,
+                                                           a_row_index=gather, f32=False,
+                                                           y_bf16=y), reps, warm)
+        xg = act[0].index_select(0, tok_t.long()) if gather is not None else act[0]
+        tb = time_ms(torch, lambda i: nv.bf16_gemm_baseline(xg, w, group_offsets=off_t,
+                                                            f32=False), reps, warm)
+        bounds = offsets.tolist()
+
+        def blas(i):
+            for e in range(wl.experts):
+                torch.matmul(xg[bounds[e]:bounds[e + 1]], w[e].t())
+        th = time_ms(torch, blas, max(3, reps // 2), 1)
+        res["gemms"].append({"gemm": name, "m": mm, "n": nn, "k": kk, "groups": wl.experts,
+                             "w4a4_ms": round(t4, 4),
+                             "tflops": round(fl / (t4 * 1e-3) / 1e12, 1),
+                             "frac_of_f16_mfma_peak": round(fl / (t4 * 1e-3) / 1e12 /
+                                                            MFMA_F16_PEAK_TFLOPS, 4),
+                             "bf16_ms": round(tb, 4), "hipblaslt_per_expert_ms": round(th, 4),
+                             "speedup_vs_bf16": round(tb / t4, 3),
+                             "speedup_vs_hipblaslt": round(th / t4, 3)})
+        layer["w4a4_ms"] += t4
+        layer["bf16_ms"] += tb
+        layer["hipblaslt_ms"] += th
+        log(f"  {name} grouped {mm}x{nn}x{kk}: w4a4 {t4:.3f} ms, bf16 {tb:.3f} ms, "
+            f"hipBLASLt per expert {th:.3f} ms")
+        del w, qws, b_codes, b_scales, y, xg
+        torch.cuda.empty_cache()
+    layer["speedup_vs_bf16"] = round(layer["bf16_ms"] / layer["w4a4_ms"], 3)
+    layer["speedup_vs_hipblaslt"] = round(layer["hipblaslt_ms"] / layer["w4a4_ms"], 3)
+    res["layer"] = {k: round(v, 4) for k, v in layer.items()}
+    return res
 
 
 def cpu_baseline(wl, x_host, w_host, rows, flops_step, m):
