@@ -504,87 +504,93 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   }
 
   // ---- epilogue ------------------------------------------------------------
-  // The accumulators leave through LDS, one 32-row band (i) of the wave's
-  // tile at a time: the lanes write their values in the MFMA layout, then
-  // each lane reads back 16 contiguous bytes of one output row and stores
-  // them with one vector store.  Each wave has a region of its own in the
-  // (now idle) ring; a wave's LDS operations complete in order, so the band
-  // needs no barrier between its writes and reads.
+  // The accumulators leave through LDS, 16 rows of the wave's tile (a band)
+  // at a time.  Each value is read once and scaled; the lanes write it in the
+  // MFMA layout to a float32 band and/or a BF16 band (rounded two rows at a
+  // time by the hardware's RNE conversion), then each lane reads back 16
+  // contiguous bytes of one output row and stores them.  Each wave has a
+  // region of its own in the (now idle) ring; a wave's LDS operations
+  // complete in order, so a band needs no barrier between writes and reads.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no DMA still writing the ring
   __syncthreads();                         // every wave is done with the ring
   const float scale = (*p.alpha_a) * p.alpha_b[tc.group] * 256.0f;
   const int64_t row_lim = tc.m0 + BM < tc.m_end ? tc.m0 + BM : tc.m_end;
+  const bool want32 = p.y_f32 != nullptr, want16 = p.y_bf16 != nullptr;
+  constexpr int kBandRows = 16;
   constexpr int kPitch32 = WN * 4 + 32, kPitch16 = WN * 2 + 16;   // padded rows
-  static_assert(4 * 32 * kPitch32 <= kRing * kStageBytes, "epilogue bands fit the ring");
-  uint8_t* band = lds + wave * 32 * kPitch32;
+  constexpr int kBandBytes = kBandRows * (kPitch32 + kPitch16);
+  static_assert(4 * kBandBytes <= kRing * kStageBytes, "epilogue bands fit the ring");
+  uint8_t* band32 = lds + wave * kBandBytes;
+  uint8_t* band16 = band32 + kBandRows * kPitch32;
+  const bool interior = tc.m0 + BM <= tc.m_end && tc.n0 + BN <= p.N;
 
-  // Writes band i into LDS: float32 values one by one, BF16 values rounded
-  // two at a time (rows R and R + 1 of a column) by the hardware's RNE
-  // conversion.
-  auto band_f32 = [&](int i) __attribute__((always_inline)) {
+  // Band (i, h): rows 16h .. 16h + 15 of fragment row i, i.e. accumulator
+  // registers r = 8h .. 8h + 7 (row 8(r/4) + 4(lane/32) + r%4).
+  auto band_write = [&](int i, int h) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * fh + (r & 3);
-        *reinterpret_cast<float*>(band + row * kPitch32 + (32 * j + fr) * 4) =
-            acc[i][j][r] * scale;
+      for (int r = 8 * h; r < 8 * h + 8; r += 2) {
+        const int row = 8 * ((r >> 2) - 2 * h) + 4 * fh + (r & 3);
+        const float v0 = acc[i][j][r] * scale, v1 = acc[i][j][r + 1] * scale;
+        if (want32) {
+          float* d = reinterpret_cast<float*>(band32 + row * kPitch32 + (32 * j + fr) * 4);
+          d[0] = v0;
+          d[kPitch32 / 4] = v1;
+        }
+        if (want16) {
+          const bf16x2_t b = __builtin_convertvector((float2_t){v0, v1}, bf16x2_t);
+          __bf16* d = reinterpret_cast<__bf16*>(band16 + row * kPitch16 + (32 * j + fr) * 2);
+          d[0] = b[0];
+          d[kPitch16 / 2] = b[1];
+        }
       }
   };
-  auto band_bf16 = [&](int i) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const int row = 8 * (r >> 2) + 4 * fh + (r & 3);
-        const bf16x2_t h = __builtin_convertvector(
-            (float2_t){acc[i][j][r] * scale, acc[i][j][r + 1] * scale}, bf16x2_t);
-        __bf16* dst = reinterpret_cast<__bf16*>(band + row * kPitch16 + (32 * j + fr) * 2);
-        dst[0] = h[0];
-        dst[kPitch16 / 2] = h[1];
-      }
-  };
-  // Reads band i back in 16-byte row chunks and stores them.
-  auto band_store = [&](auto* y, int vec, int i) __attribute__((always_inline)) {
+  // Stores band (i, h) of one output: straight-line 16-byte stores when the
+  // tile is inside the output and rows are 16-byte aligned (uniform test),
+  // else element by element with bounds checks.
+  auto band_store = [&](auto* y, const uint8_t* band, int vec, int i, int h)
+      __attribute__((always_inline)) {
     using T = typename std::remove_pointer<decltype(y)>::type;
     constexpr int kE = (int)sizeof(T), kPitch = kE == 4 ? kPitch32 : kPitch16;
     constexpr int kPer = 16 / kE;                    // elements per 16-byte chunk
-    constexpr int kChunks = 32 * WN / kPer;          // chunks in a band
+    constexpr int kChunks = kBandRows * WN / kPer;   // chunks in a band
+    const int64_t row0 = tc.m0 + wm + 32 * i + kBandRows * h;
+    T* y_band = y + row0 * p.ld_y + tc.n0 + wn;
+    if (interior && vec) {
 #pragma unroll
-    for (int q = 0; q < kChunks / 64; ++q) {
-      const int e = (q * 64 + lane) * kPer;
-      const int row = e / WN, col = e % WN;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(band + row * kPitch + col * kE);
-      const int64_t grow = tc.m0 + wm + 32 * i + row;
-      const int64_t gcol = tc.n0 + wn + col;
-      if (grow < row_lim) {
-        T* dst = y + grow * p.ld_y + gcol;
-        if (vec && gcol + kPer <= p.N) {
-          *reinterpret_cast<u32x4*>(dst) = v;
-        } else {
-          const T* t = reinterpret_cast<const T*>(&v);
-#pragma unroll
+      for (int q = 0; q < kChunks / 64; ++q) {
+        const int e = (q * 64 + lane) * kPer;
+        const int row = e / WN, col = e % WN;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(band + row * kPitch + col * kE);
+        *reinterpret_cast<u32x4*>(y_band + row * p.ld_y + col) = v;
+      }
+    } else {
+      const int64_t rows_left = row_lim - row0;
+      const int64_t cols_left = p.N - (tc.n0 + wn);
+#pragma unroll 1
+      for (int q = 0; q < kChunks / 64; ++q) {
+        const int e = (q * 64 + lane) * kPer;
+        const int row = e / WN, col = e % WN;
+        const T* src = reinterpret_cast<const T*>(band + row * kPitch + col * kE);
+        if (row < rows_left) {
+#pragma unroll 1
           for (int k = 0; k < kPer; ++k)
-            if (gcol + k < p.N) dst[k] = t[k];
+            if (col + k < cols_left) y_band[row * p.ld_y + col + k] = src[k];
         }
       }
     }
   };
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    if (p.y_f32) {
-      band_f32(i);
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      band_write(i, h);
       __builtin_amdgcn_wave_barrier();
-      band_store(p.y_f32, p.vec_f32, i);
-      __builtin_amdgcn_wave_barrier();
-    }
-    if (p.y_bf16) {
-      band_bf16(i);
-      __builtin_amdgcn_wave_barrier();
-      band_store(reinterpret_cast<__bf16*>(p.y_bf16), p.vec_bf16, i);
+      if (want32) band_store(p.y_f32, band32, p.vec_f32, i, h);
+      if (want16) band_store(reinterpret_cast<__bf16*>(p.y_bf16), band16, p.vec_bf16, i, h);
       __builtin_amdgcn_wave_barrier();
     }
-  }
 }
 
 template <int BM, int BN, bool kFused, int kRing, int kOcc>
