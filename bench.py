@@ -6,7 +6,8 @@ tokens, hidden 4096: Q 4096->4096, K and V 4096->1024, O 4096->4096.  One
 step is one pass of the whole hot path over one batch:
 
     alpha + NVFP4 quantisation of X_qkv   (amax, prepare, quantize kernels)
-    Q, K, V W4A4 GEMMs (BF16 outputs)
+    Q, K, V W4A4 GEMMs as one launch over the stacked weights (each keeps
+        its own tensor scale; BF16 output [8192, 6144])
     alpha + NVFP4 quantisation of X_o
     O W4A4 GEMM
 
@@ -15,7 +16,8 @@ inputs of consecutive steps rotate over several copies whose total exceeds the
 256 MB last-level cache, so every step reads its activations from HBM.
 
 The same step with the BF16 comparison GEMM (no quantisation) and with
-torch.matmul (hipBLASLt) gives the speedups.  The oracle is timed on a
+torch.matmul (hipBLASLt), both also over the stacked Q|K|V weights, gives the
+speedups.  The oracle is timed on a
 bounded sample on the host cores.  One JSON line goes to stdout.
 """
 from __future__ import annotations
@@ -34,7 +36,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0          # dense f16/bf16 MFMA, MI355X
 HBM_PEAK_GBPS = 8000.0
 QUANT_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 16.0   # read BF16, write codes + scales
 AMAX_BYTES_PER_ELEM = 2.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a4_gemm_256x256_qwen3_8b_attn_m8192_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a4_gemm_qkv_8192x6144x4096_traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "nvfp4_w4a4_gemm_amd", "csrc", "gemm_w4a4.hip")
 
 
@@ -144,50 +146,46 @@ def main():
     ws = {k: nv.to_device_bf16(v, dev) for k, v in w_host.items()}
     workspace = nv.new_workspace(dev)
     wq = {k: nv.nvfp4_quantize_weights(v, workspace=workspace) for k, v in ws.items()}
+    qkv = nv.stack_tensors([wq["W_q"], wq["W_k"], wq["W_v"]])
+    w_qkv = torch.cat([ws["W_q"], ws["W_k"], ws["W_v"]], dim=0).contiguous()
+    n_qkv = qkv.rows
     qbuf = {k: nv.nvfp4_quantize_act(xs[0][k], workspace=workspace) for k in x_host}
-    outs = {g: torch.empty(m, wq[w].rows, dtype=torch.bfloat16, device=dev)
-            for g, w in (("q", "W_q"), ("k", "W_k"), ("v", "W_v"), ("o", "W_o"))}
+    outs = {"qkv": torch.empty(m, n_qkv, dtype=torch.bfloat16, device=dev),
+            "o": torch.empty(m, h, dtype=torch.bfloat16, device=dev)}
     torch.cuda.synchronize()
 
-    proj = (("q", "W_q"), ("k", "W_k"), ("v", "W_v"))
-    flops_step = sum(2.0 * m * wq[w].rows * h for _, w in proj) + 2.0 * m * h * h
+    flops_qkv = 2.0 * m * n_qkv * h
+    flops_o = 2.0 * m * h * h
+    flops_step = flops_qkv + flops_o
     timer = Timer(torch)
+
+    class _Null:
+        def __enter__(self):
+            return None
+
+        def __exit__(self, *a):
+            return False
 
     def w4a4_step(i, timed):
         x = xs[i % args.rotate]
-        ctx = timer if timed else None
-        for name, key in (("quant_qkv", "X_qkv"),):
-            if ctx:
-                with ctx("quantize"):
-                    nv.nvfp4_quantize_act(x[key], out=qbuf[key], workspace=workspace)
-            else:
-                nv.nvfp4_quantize_act(x[key], out=qbuf[key], workspace=workspace)
-        for g, w in proj:
-            kname = "gemm_big" if g == "q" else "gemm_small"
-            if ctx:
-                with ctx(kname):
-                    nv.w4a4_gemm(qbuf["X_qkv"], wq[w], f32=False, y_bf16=outs[g])
-            else:
-                nv.w4a4_gemm(qbuf["X_qkv"], wq[w], f32=False, y_bf16=outs[g])
-        if ctx:
-            with ctx("quantize"):
-                nv.nvfp4_quantize_act(x["X_o"], out=qbuf["X_o"], workspace=workspace)
-            with ctx("gemm_big"):
-                nv.w4a4_gemm(qbuf["X_o"], wq["W_o"], f32=False, y_bf16=outs["o"])
-        else:
+        ctx = timer if timed else (lambda name: _Null())
+        with ctx("quantize"):
+            nv.nvfp4_quantize_act(x["X_qkv"], out=qbuf["X_qkv"], workspace=workspace)
+        with ctx("gemm_qkv"):
+            nv.w4a4_gemm_multi(qbuf["X_qkv"], qkv, f32=False, y_bf16=outs["qkv"])
+        with ctx("quantize"):
             nv.nvfp4_quantize_act(x["X_o"], out=qbuf["X_o"], workspace=workspace)
+        with ctx("gemm_o"):
             nv.w4a4_gemm(qbuf["X_o"], wq["W_o"], f32=False, y_bf16=outs["o"])
 
     def bf16_step(i):
         x = xs[i % args.rotate]
-        for g, w in proj:
-            nv.bf16_gemm_baseline(x["X_qkv"], ws[w], f32=False)
+        nv.bf16_gemm_baseline(x["X_qkv"], w_qkv, f32=False)
         nv.bf16_gemm_baseline(x["X_o"], ws["W_o"], f32=False)
 
     def blas_step(i):
         x = xs[i % args.rotate]
-        for g, w in proj:
-            torch.matmul(x["X_qkv"], ws[w].t())
+        torch.matmul(x["X_qkv"], w_qkv.t())
         torch.matmul(x["X_o"], ws["W_o"].t())
 
     def time_steps(fn, steps, warmup):
@@ -212,17 +210,16 @@ def main():
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t) * 1e3 / args.steps
 
-    n_big = timer.count("gemm_big")
-    big_ms = timer.total_ms("gemm_big") / n_big
-    small_ms = timer.total_ms("gemm_small") / max(1, timer.count("gemm_small"))
+    qkv_ms = timer.total_ms("gemm_qkv") / timer.count("gemm_qkv")
+    o_ms = timer.total_ms("gemm_o") / timer.count("gemm_o")
     quant_ms = timer.total_ms("quantize") / timer.count("quantize")
-    gemm_ms_step = (timer.total_ms("gemm_big") + timer.total_ms("gemm_small")) / args.steps
-    big_flops = 2.0 * m * h * h
-    big_tflops = big_flops / (big_ms * 1e-3) / 1e12
+    gemm_ms_step = qkv_ms + o_ms
+    qkv_tflops = flops_qkv / (qkv_ms * 1e-3) / 1e12
+    o_tflops = flops_o / (o_ms * 1e-3) / 1e12
     quant_bytes = m * h * (QUANT_BYTES_PER_ELEM + AMAX_BYTES_PER_ELEM)
     quant_gbps = quant_bytes / (quant_ms * 1e-3) / 1e9
-    log(f"W4A4 step {ms_step:.3f} ms; GEMM 8192x4096x4096 {big_ms:.3f} ms "
-        f"({big_tflops:.0f} TFLOP/s); K/V GEMM {small_ms:.3f} ms; "
+    log(f"W4A4 step {ms_step:.3f} ms; GEMM Q|K|V {m}x{n_qkv}x{h} {qkv_ms:.3f} ms "
+        f"({qkv_tflops:.0f} TFLOP/s); GEMM O {m}x{h}x{h} {o_ms:.3f} ms ({o_tflops:.0f} TFLOP/s); "
         f"quantize {quant_ms:.3f} ms ({quant_gbps:.0f} GB/s incl. amax)")
 
     # --- quantiser passes on their own, and the attainable copy rate ----------
@@ -267,19 +264,20 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "Qwen3-8B-shaped attention projections at prefill: M=8192, hidden 4096, "
-                        "Q 4096->4096, K/V 4096->1024, O 4096->4096; NVFP4 W4A4, BF16 out",
+                        "Q 4096->4096, K/V 4096->1024 (one launch over the stacked Q|K|V "
+                        "weights), O 4096->4096; NVFP4 W4A4, BF16 out",
             "global_batch": m,
             "flops_per_step": flops_step,
             "parallelism": "single GPU",
             "input_rotation": args.rotate,
         },
         "roofline": {
-            "kernel": "w4a4_gemm_kernel<256,256> (Q and O projections, 8192x4096x4096)",
+            "kernel": f"w4a4_gemm_kernel<256,256> (stacked Q|K|V projection, {m}x{n_qkv}x{h})",
             "bound": "mfma",
-            "achieved": round(big_tflops, 2),
+            "achieved": round(qkv_tflops, 2),
             "peak": MFMA_F16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(big_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+            "frac": round(qkv_tflops / MFMA_F16_PEAK_TFLOPS, 4),
             "traffic": traffic,
         },
         "quantize": {
@@ -293,7 +291,8 @@ def main():
         },
         "gemm": {"ms_per_step": round(gemm_ms_step, 4),
                  "tflops": round(flops_step / (gemm_ms_step * 1e-3) / 1e12, 2),
-                 "kv_gemm_ms": round(small_ms, 4)},
+                 "qkv_ms": round(qkv_ms, 4), "o_ms": round(o_ms, 4),
+                 "o_tflops": round(o_tflops, 2)},
         "bf16_baseline": {"ms_per_step": round(bf16_ms, 4),
                           "speedup_layer": round(bf16_ms / ms_step, 3),
                           "speedup_gemm_only": round(bf16_ms / gemm_ms_step, 3),

@@ -131,6 +131,25 @@ nvfp4_status_t w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                          uint16_t* y_bf16, int64_t ld_y, hipStream_t stream);
 
 /*
+ * w4a4_gemm_multi - w4a4_gemm where the weight operand is several NVFP4
+ * tensors stacked along N, each quantised under its own tensor scale (for
+ * example the Q, K and V projections of one activation, 核心方法 "W4A4"
+ * linear layers of the paper.rainbus digest, run as one launch):
+ *
+ *   b_codes/b_scales  the tensors' rows concatenated, [N][K/2], [N][K/16]
+ *   alpha_b_rows      device float32 [N]: the tensor scale of each B row
+ *
+ * Output column n is scaled by alpha_a * alpha_b_rows[n]; every output is
+ * bit-identical to w4a4_gemm on that row's own tensor.  Other arguments,
+ * ownership and errors as for w4a4_gemm.
+ */
+nvfp4_status_t w4a4_gemm_multi(const uint8_t* a_codes, const uint8_t* a_scales,
+                               const float* alpha_a, const uint8_t* b_codes,
+                               const uint8_t* b_scales, const float* alpha_b_rows,
+                               int64_t M, int64_t N, int64_t K, float* y_f32,
+                               uint16_t* y_bf16, int64_t ld_y, hipStream_t stream);
+
+/*
  * w4a4_gemm_grouped - the W4A4 GEMM of a mixture-of-experts layer: one
  * launch over num_groups experts with ragged row counts.
  *

@@ -30,6 +30,8 @@ _SIGNATURES = {
                            _c_void],
     "w4a4_gemm": [_c_void, _c_void, _c_void, _c_void, _c_void, _c_void, _c_i64, _c_i64,
                   _c_i64, _c_void, _c_void, _c_i64, _c_void],
+    "w4a4_gemm_multi": [_c_void, _c_void, _c_void, _c_void, _c_void, _c_void, _c_i64, _c_i64,
+                        _c_i64, _c_void, _c_void, _c_i64, _c_void],
     "w4a4_gemm_grouped": [_c_void, _c_void, _c_void, _c_i64, _c_void, _c_void, _c_void,
                           _c_void, _c_i64, _c_i64, _c_i64, _c_i32, _c_void, _c_void,
                           _c_void, _c_i64, _c_void],
@@ -189,6 +191,50 @@ def w4a4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, f32: bool = True, bf16: bool = Tru
     ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
     _call("w4a4_gemm", _ptr(a.codes), _ptr(a.scales), _ptr(a.alpha), _ptr(b.codes),
           _ptr(b.scales), _ptr(b.alpha), m, n, k, _ptr(y_f32), _ptr(y_bf16), ld,
+          _stream(a.codes.device))
+    return y_f32, y_bf16
+
+
+@dataclass
+class NVFP4Stack:
+    """Several NVFP4 tensors of the same K stacked along rows (e.g. Q, K, V
+    weights): codes [N, K/2], scales [N, K/16], alpha_rows [N] (float32)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    alpha_rows: torch.Tensor
+    offsets: list
+
+    @property
+    def rows(self) -> int:
+        return self.codes.shape[0]
+
+    @property
+    def k(self) -> int:
+        return self.codes.shape[1] * 2
+
+
+def stack_tensors(parts) -> NVFP4Stack:
+    """Concatenate quantised tensors along rows, each keeping its own alpha."""
+    codes = torch.cat([t.codes for t in parts], dim=0)
+    scales = torch.cat([t.scales for t in parts], dim=0)
+    alpha_rows = torch.cat([t.alpha.expand(t.rows) for t in parts]).contiguous()
+    offsets = [0]
+    for t in parts:
+        offsets.append(offsets[-1] + t.rows)
+    return NVFP4Stack(codes, scales, alpha_rows, offsets)
+
+
+def w4a4_gemm_multi(a: NVFP4Tensor, b: NVFP4Stack, f32: bool = True, bf16: bool = True,
+                    y_f32: torch.Tensor | None = None, y_bf16: torch.Tensor | None = None):
+    """W4A4 GEMM against stacked weights; column n is scaled by b.alpha_rows[n]."""
+    m, k = a.rows, a.k
+    n = b.rows
+    if b.k != k:
+        raise ValueError("operands disagree on K")
+    y_f32, y_bf16 = _outputs(m, n, a.codes.device, f32, bf16, y_f32, y_bf16)
+    ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
+    _call("w4a4_gemm_multi", _ptr(a.codes), _ptr(a.scales), _ptr(a.alpha), _ptr(b.codes),
+          _ptr(b.scales), _ptr(b.alpha_rows), m, n, k, _ptr(y_f32), _ptr(y_bf16), ld,
           _stream(a.codes.device))
     return y_f32, y_bf16
 

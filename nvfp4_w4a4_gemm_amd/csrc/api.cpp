@@ -163,7 +163,8 @@ nvfp4_status_t nvfp4_tensor_alpha(const void* x_bf16, int64_t M, int64_t K, int6
 static nvfp4_status_t gemm_common(const uint8_t* a_codes, const uint8_t* a_scales,
                                   const float* alpha_a, int64_t a_rows,
                                   const int32_t* a_row_index, const uint8_t* b_codes,
-                                  const uint8_t* b_scales, const float* alpha_b, int64_t M,
+                                  const uint8_t* b_scales, const float* alpha_b,
+                                  const float* alpha_b_rows, int64_t M,
                                   int64_t N, int64_t K, int32_t num_groups,
                                   const int64_t* group_offsets, float* y_f32, uint16_t* y_bf16,
                                   int64_t ld_y, hipStream_t stream) {
@@ -174,7 +175,7 @@ static nvfp4_status_t gemm_common(const uint8_t* a_codes, const uint8_t* a_scale
   nvfp4_status_t st = check_outputs(y_f32, y_bf16, N, ld_y);
   if (st != NVFP4_OK) return st;
   if (M == 0 || N == 0) return NVFP4_OK;
-  if (!a_codes || !a_scales || !alpha_a || !b_codes || !b_scales || !alpha_b)
+  if (!a_codes || !a_scales || !alpha_a || !b_codes || !b_scales || !(alpha_b || alpha_b_rows))
     return NVFP4_ERR_NULL;
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16)) return NVFP4_ERR_ALIGN;
   if (K % 128 == 0 && (!aligned(a_scales, 8) || !aligned(b_scales, 8))) return NVFP4_ERR_ALIGN;
@@ -192,6 +193,7 @@ static nvfp4_status_t gemm_common(const uint8_t* a_codes, const uint8_t* a_scale
   a.b_codes = b_codes;
   a.b_scales = b_scales;
   a.alpha_b = alpha_b;
+  a.alpha_b_rows = alpha_b_rows;
   a.M = M;
   a.N = N;
   a.K = K;
@@ -210,8 +212,18 @@ nvfp4_status_t w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const 
                          const uint8_t* b_codes, const uint8_t* b_scales, const float* alpha_b,
                          int64_t M, int64_t N, int64_t K, float* y_f32, uint16_t* y_bf16,
                          int64_t ld_y, hipStream_t stream) {
-  return gemm_common(a_codes, a_scales, alpha_a, M, nullptr, b_codes, b_scales, alpha_b, M, N,
-                     K, 1, nullptr, y_f32, y_bf16, ld_y, stream);
+  return gemm_common(a_codes, a_scales, alpha_a, M, nullptr, b_codes, b_scales, alpha_b, nullptr,
+                     M, N, K, 1, nullptr, y_f32, y_bf16, ld_y, stream);
+}
+
+nvfp4_status_t w4a4_gemm_multi(const uint8_t* a_codes, const uint8_t* a_scales,
+                               const float* alpha_a, const uint8_t* b_codes,
+                               const uint8_t* b_scales, const float* alpha_b_rows, int64_t M,
+                               int64_t N, int64_t K, float* y_f32, uint16_t* y_bf16,
+                               int64_t ld_y, hipStream_t stream) {
+  if (alpha_b_rows == nullptr) return NVFP4_ERR_NULL;
+  return gemm_common(a_codes, a_scales, alpha_a, M, nullptr, b_codes, b_scales, nullptr,
+                     alpha_b_rows, M, N, K, 1, nullptr, y_f32, y_bf16, ld_y, stream);
 }
 
 nvfp4_status_t w4a4_gemm_grouped(const uint8_t* a_codes, const uint8_t* a_scales,
@@ -222,8 +234,10 @@ nvfp4_status_t w4a4_gemm_grouped(const uint8_t* a_codes, const uint8_t* a_scales
                                  const int64_t* group_offsets, float* y_f32, uint16_t* y_bf16,
                                  int64_t ld_y, hipStream_t stream) {
   if (group_offsets == nullptr) return NVFP4_ERR_NULL;
+  if (alpha_b == nullptr) return NVFP4_ERR_NULL;
   return gemm_common(a_codes, a_scales, alpha_a, a_rows, a_row_index, b_codes, b_scales,
-                     alpha_b, M, N, K, num_groups, group_offsets, y_f32, y_bf16, ld_y, stream);
+                     alpha_b, nullptr, M, N, K, num_groups, group_offsets, y_f32, y_bf16, ld_y,
+                     stream);
 }
 
 nvfp4_status_t w4a4_gemm_fused_act(const void* x_bf16, int64_t ld_x, const float* alpha_a,
@@ -257,6 +271,7 @@ nvfp4_status_t w4a4_gemm_fused_act(const void* x_bf16, int64_t ld_x, const float
   a.b_codes = b_codes;
   a.b_scales = b_scales;
   a.alpha_b = alpha_b;
+  a.alpha_b_rows = nullptr;
   a.M = M;
   a.N = N;
   a.K = K;

@@ -513,7 +513,20 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   // complete in order, so a band needs no barrier between writes and reads.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no DMA still writing the ring
   __syncthreads();                         // every wave is done with the ring
-  const float scale = (*p.alpha_a) * p.alpha_b[tc.group] * 256.0f;
+  // alpha_a alpha_b 2^8 per fragment column (one alpha_b per B row when B
+  // concatenates several tensors, else the group's)
+  float scale[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    float ab;
+    if (p.alpha_b_rows) {
+      const int64_t col = tc.n0 + wn + 32 * j + fr;
+      ab = p.alpha_b_rows[col < p.N ? col : p.N - 1];
+    } else {
+      ab = p.alpha_b[tc.group];
+    }
+    scale[j] = (*p.alpha_a) * ab * 256.0f;
+  }
   const int64_t row_lim = tc.m0 + BM < tc.m_end ? tc.m0 + BM : tc.m_end;
   const bool want32 = p.y_f32 != nullptr, want16 = p.y_bf16 != nullptr;
   constexpr int kBandRows = 16;
@@ -532,7 +545,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
 #pragma unroll
       for (int r = 8 * h; r < 8 * h + 8; r += 2) {
         const int row = 8 * ((r >> 2) - 2 * h) + 4 * fh + (r & 3);
-        const float v0 = acc[i][j][r] * scale, v1 = acc[i][j][r + 1] * scale;
+        const float v0 = acc[i][j][r] * scale[j], v1 = acc[i][j][r + 1] * scale[j];
         if (want32) {
           float* d = reinterpret_cast<float*>(band32 + row * kPitch32 + (32 * j + fr) * 4);
           d[0] = v0;

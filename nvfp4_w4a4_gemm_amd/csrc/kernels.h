@@ -58,6 +58,7 @@ struct W4A4Args {
   const uint8_t* b_codes;
   const uint8_t* b_scales;
   const float* alpha_b;
+  const float* alpha_b_rows;      // nullable: tensor scale of each B row [N]
   int64_t M, N, K;
   int32_t num_groups;             // 1 for a dense GEMM
   const int64_t* group_offsets;   // device [num_groups + 1] or nullptr

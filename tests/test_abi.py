@@ -32,7 +32,8 @@ def header_functions():
 
 def test_header_declares_the_four_entry_points():
     names = header_functions()
-    for n in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "w4a4_gemm", "bf16_gemm_baseline"):
+    for n in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "w4a4_gemm", "bf16_gemm_baseline",
+              "w4a4_gemm_multi", "w4a4_gemm_grouped", "w4a4_gemm_fused_act"):
         assert n in names
 
 
@@ -122,6 +123,20 @@ def test_gemm_validation(lib):
     assert f(*bad) == NULL
     zero = list(args); zero[6] = 0                            # M = 0: nothing to do
     assert f(*zero) == OK
+
+
+@needs_lib
+def test_gemm_multi_validation(lib):
+    f = lib.w4a4_gemm_multi
+    # a_codes, a_scales, alpha_a, b_codes, b_scales, alpha_b_rows, M, N, K, y32, y16, ld, stream
+    args = [p(), p(), p(), p(), p(), p(), 64, 96, 256, p(), p(), 96, None]
+    assert f(*args) == UNSUPPORTED
+    bad = list(args); bad[5] = None                           # per-row scales required
+    assert f(*bad) == NULL
+    bad = list(args); bad[8] = 24
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[3] = p(4)
+    assert f(*bad) == ALIGN
 
 
 @needs_lib

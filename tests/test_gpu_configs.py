@@ -107,7 +107,7 @@ def check_gemm(name, a, w, seed, a_rows_of_output=None, out_rows=None):
 def test_dense_config(cfg):
     wl = workload(cfg)
     print(f"\n[cfg {cfg}] {wl.title}: generating", flush=True)
-    acts, wts = {}, {}
+    acts, wts, keep = {}, {}, {}
     for i, g in enumerate(wl.gemms):
         if g.act not in acts:
             acts[g.act] = Quantized(g.act, wl.tensors[g.act].full(), False, 100 * cfg + i)
@@ -124,8 +124,19 @@ def test_dense_config(cfg):
             torch.cuda.synchronize()
             assert torch.equal(f16.view(torch.int16), y16.view(torch.int16)), g.name
             print(f"[cfg 4 {g.name}] fused quantise-on-load GEMM bit-identical", flush=True)
+        if cfg == 2 and g.name != "o_proj":
+            keep[g.weight] = (wts[g.weight].q, y16)
         del wts[g.weight]
         torch.cuda.empty_cache()
+    if cfg == 2:
+        # Q, K and V as one launch over the stacked weights: bit-identical
+        stack = nv.stack_tensors([keep[w][0] for w in ("W_q", "W_k", "W_v")])
+        _, y16 = nv.w4a4_gemm_multi(acts["X_qkv"].q, stack, f32=False)
+        torch.cuda.synchronize()
+        for w, lo, hi in zip(("W_q", "W_k", "W_v"), stack.offsets[:-1], stack.offsets[1:]):
+            assert torch.equal(y16[:, lo:hi].contiguous().view(torch.int16),
+                               keep[w][1].view(torch.int16)), w
+        print("[cfg 2] Q|K|V stacked GEMM bit-identical to the three GEMMs", flush=True)
 
 
 def test_grouped_moe_config():

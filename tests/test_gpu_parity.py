@@ -221,6 +221,27 @@ def test_w4a4_gemm_large_tile_path():
     assert_gemm_close(y32[rows], y16[rows], y, bound, y16_ref)
 
 
+def test_w4a4_gemm_multi_equals_separate_gemms():
+    """Q, K, V-like weights of different magnitude (so different alphas)
+    stacked along N: every output equals its own tensor's GEMM bit for bit,
+    and matches the oracle."""
+    m, k = 300, 512
+    xb = normal_bits(m, k, seed=71)
+    parts = [normal_bits(n, k, seed=72 + i, std=std, outliers=False)
+             for i, (n, std) in enumerate(((256, 0.02), (96, 0.5), (130, 3.0)))]
+    qa = nv.nvfp4_quantize_act(dev_bf16(xb))
+    qws = [nv.nvfp4_quantize_weights(dev_bf16(w)) for w in parts]
+    stack = nv.stack_tensors(qws)
+    y32, y16 = nv.w4a4_gemm_multi(qa, stack)
+    ra = orc.quantize(xb)
+    for q, w, lo, hi in zip(qws, parts, stack.offsets[:-1], stack.offsets[1:]):
+        s32, s16 = nv.w4a4_gemm(qa, q)
+        assert torch.equal(y32[:, lo:hi], s32)
+        assert torch.equal(y16[:, lo:hi].view(torch.int16), s16.view(torch.int16))
+        y, bound, y16_ref = orc.w4a4_reference(ra, orc.quantize(w))
+        assert_gemm_close(y32[:, lo:hi], y16[:, lo:hi], y, bound, y16_ref)
+
+
 def test_w4a4_gemm_deterministic():
     xb, wb = quantized_pair(300, 300, 512, seed=31)
     qa = nv.nvfp4_quantize_act(dev_bf16(xb))
