@@ -412,13 +412,16 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ad[i], bd[j], acc[i][j], 0, 0, 0);
   };
   // one MFMA, then a quarter of the next step's decode, and so on; the
-  // group's share of the stage DMA goes after its first MFMAs
-  auto interleave = [&](int n_dma = 0) __attribute__((always_inline)) {
+  // group's share of the stage DMA goes after its first MFMAs, and LDS reads
+  // (ds_lo <= MFMA index < ds_hi) one per MFMA, so no burst of loads holds
+  // up the in-order issue of the next MFMA
+  auto interleave = [&](int n_dma = 0, int ds_lo = 0, int ds_hi = 0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TM * TN; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i < n_dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      if (i >= ds_lo && i < ds_hi) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -476,9 +479,9 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
       __builtin_amdgcn_s_barrier();
     }
     read_half0(nbuf);                       // next stage: words of steps 0-3, scales
-    __builtin_amdgcn_sched_group_barrier(0x100, kHalf0Reads, 0);
     nd = dma_group(kt, 3);
-    decode_step(4, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);  interleave(nd);
+    decode_step(4, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);
+    interleave(nd, 0, kHalf0Reads);
     nd = dma_group(kt, 4);
     decode_step(5, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave(nd);
     nd = dma_group(kt, 5);
@@ -487,14 +490,8 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
     // decoded (consumed at the next stage's step 3)
     decode_step(7, a_nxt, b_nxt);
     mfma_step(a_cur, b_cur);
-#pragma unroll
-    for (int i = 0; i < TM * TN; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-    }
     read_half1(nbuf);
-    __builtin_amdgcn_sched_group_barrier(0x100, kHalf1Reads, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    interleave(0, TM * TN - kHalf1Reads, TM * TN);
     // step 7: decode the next stage's step 0 (its first half and scales are
     // in registers since step 3) under this stage's last MFMAs
     decode_with(0, a_cur, b_cur, asn, bsn);
