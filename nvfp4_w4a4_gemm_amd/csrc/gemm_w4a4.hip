@@ -535,72 +535,84 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   const bool interior = tc.m0 + BM <= tc.m_end && tc.n0 + BN <= p.N;
 
   // Band (i, h): rows 16h .. 16h + 15 of fragment row i, i.e. accumulator
-  // registers r = 8h .. 8h + 7 (row 8(r/4) + 4(lane/32) + r%4).
-  auto band_write = [&](int i, int h) __attribute__((always_inline)) {
+  // registers r = 8h .. 8h + 7 (row 8(r/4) + 4(lane/32) + r%4).  Each lane
+  // writes at a fixed base plus compile-time offsets.
+  uint8_t* w32 = band32 + (4 * fh) * kPitch32 + fr * 4;
+  uint8_t* w16 = band16 + (4 * fh) * kPitch16 + fr * 2;
+  auto band_write = [&](int i, int h, auto k32, auto k16) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 8 * h; r < 8 * h + 8; r += 2) {
-        const int row = 8 * ((r >> 2) - 2 * h) + 4 * fh + (r & 3);
+        const int row = 8 * ((r >> 2) - 2 * h) + (r & 3);
         const float v0 = acc[i][j][r] * scale[j], v1 = acc[i][j][r + 1] * scale[j];
-        if (want32) {
-          float* d = reinterpret_cast<float*>(band32 + row * kPitch32 + (32 * j + fr) * 4);
-          d[0] = v0;
-          d[kPitch32 / 4] = v1;
+        if (decltype(k32)::value) {
+          *reinterpret_cast<float*>(w32 + row * kPitch32 + 32 * j * 4) = v0;
+          *reinterpret_cast<float*>(w32 + (row + 1) * kPitch32 + 32 * j * 4) = v1;
         }
-        if (want16) {
+        if (decltype(k16)::value) {
           const bf16x2_t b = __builtin_convertvector((float2_t){v0, v1}, bf16x2_t);
-          __bf16* d = reinterpret_cast<__bf16*>(band16 + row * kPitch16 + (32 * j + fr) * 2);
-          d[0] = b[0];
-          d[kPitch16 / 2] = b[1];
+          *reinterpret_cast<__bf16*>(w16 + row * kPitch16 + 32 * j * 2) = b[0];
+          *reinterpret_cast<__bf16*>(w16 + (row + 1) * kPitch16 + 32 * j * 2) = b[1];
         }
       }
   };
-  // Stores band (i, h) of one output: straight-line 16-byte stores when the
-  // tile is inside the output and rows are 16-byte aligned (uniform test),
-  // else element by element with bounds checks.
+  // Stores band (i, h) of one output.  Chunk q of a lane covers row
+  // q * kRowsPerQ + lane_row, columns lane_col .. lane_col + kPer - 1 of the
+  // band.  Straight-line 16-byte stores when the tile is inside the output
+  // and rows are 16-byte aligned (a uniform test), else element by element
+  // with bounds checks.
   auto band_store = [&](auto* y, const uint8_t* band, int vec, int i, int h)
       __attribute__((always_inline)) {
     using T = typename std::remove_pointer<decltype(y)>::type;
     constexpr int kE = (int)sizeof(T), kPitch = kE == 4 ? kPitch32 : kPitch16;
     constexpr int kPer = 16 / kE;                    // elements per 16-byte chunk
-    constexpr int kChunks = kBandRows * WN / kPer;   // chunks in a band
+    constexpr int kLanesPerRow = WN / kPer;
+    constexpr int kRowsPerQ = 64 / kLanesPerRow;
+    static_assert(64 % kLanesPerRow == 0, "a row is a whole number of lanes");
+    constexpr int kQ = kBandRows / kRowsPerQ;
+    const int lane_row = lane / kLanesPerRow, lane_col = (lane % kLanesPerRow) * kPer;
     const int64_t row0 = tc.m0 + wm + 32 * i + kBandRows * h;
-    T* y_band = y + row0 * p.ld_y + tc.n0 + wn;
+    const uint8_t* src = band + lane_row * kPitch + lane_col * kE;
+    T* dst = y + (row0 + lane_row) * p.ld_y + tc.n0 + wn + lane_col;
+    const int64_t step = (int64_t)kRowsPerQ * p.ld_y;
     if (interior && vec) {
 #pragma unroll
-      for (int q = 0; q < kChunks / 64; ++q) {
-        const int e = (q * 64 + lane) * kPer;
-        const int row = e / WN, col = e % WN;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(band + row * kPitch + col * kE);
-        *reinterpret_cast<u32x4*>(y_band + row * p.ld_y + col) = v;
-      }
+      for (int q = 0; q < kQ; ++q)
+        *reinterpret_cast<u32x4*>(dst + q * step) =
+            *reinterpret_cast<const u32x4*>(src + q * kRowsPerQ * kPitch);
     } else {
       const int64_t rows_left = row_lim - row0;
       const int64_t cols_left = p.N - (tc.n0 + wn);
 #pragma unroll 1
-      for (int q = 0; q < kChunks / 64; ++q) {
-        const int e = (q * 64 + lane) * kPer;
-        const int row = e / WN, col = e % WN;
-        const T* src = reinterpret_cast<const T*>(band + row * kPitch + col * kE);
-        if (row < rows_left) {
+      for (int q = 0; q < kQ; ++q) {
+        const T* t = reinterpret_cast<const T*>(src + q * kRowsPerQ * kPitch);
+        if (q * kRowsPerQ + lane_row < rows_left) {
 #pragma unroll 1
           for (int k = 0; k < kPer; ++k)
-            if (col + k < cols_left) y_band[row * p.ld_y + col + k] = src[k];
+            if (lane_col + k < cols_left) dst[q * step + k] = t[k];
         }
       }
     }
   };
+  auto epilogue = [&](auto k32, auto k16) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      band_write(i, h);
-      __builtin_amdgcn_wave_barrier();
-      if (want32) band_store(p.y_f32, band32, p.vec_f32, i, h);
-      if (want16) band_store(reinterpret_cast<__bf16*>(p.y_bf16), band16, p.vec_bf16, i, h);
-      __builtin_amdgcn_wave_barrier();
-    }
+      for (int h = 0; h < 2; ++h) {
+        band_write(i, h, k32, k16);
+        __builtin_amdgcn_wave_barrier();
+        if (decltype(k32)::value) band_store(p.y_f32, band32, p.vec_f32, i, h);
+        if (decltype(k16)::value)
+          band_store(reinterpret_cast<__bf16*>(p.y_bf16), band16, p.vec_bf16, i, h);
+        __builtin_amdgcn_wave_barrier();
+      }
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+  if (want32 && want16) epilogue(yes{}, yes{});
+  else if (want32) epilogue(yes{}, no{});
+  else epilogue(no{}, yes{});
 }
 
 template <int BM, int BN, bool kFused, int kRing, int kOcc>
