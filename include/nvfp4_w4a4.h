@@ -150,6 +150,36 @@ nvfp4_status_t w4a4_gemm_multi(const uint8_t* a_codes, const uint8_t* a_scales,
                                uint16_t* y_bf16, int64_t ld_y, hipStream_t stream);
 
 /*
+ * w4a4_gemm_decode - the W4A4 GEMM at decode shape: M <= 64 token rows
+ * against a whole NVFP4 weight matrix, Y = A . B^T with the same arithmetic
+ * and outputs as w4a4_gemm.  This is the decode step of the uniform-NVFP4
+ * configuration Mix-Quant is compared with (paper.rainbus digest, 实验结果,
+ * Table 1 and the phase-wise ablation of Table 3).  At this shape the time
+ * goes to reading the weight codes once, so the kernel is laid out for the
+ * HBM stream rather than for the matrix cores (one workgroup per 16 output
+ * columns).
+ *
+ *   a_codes/a_scales  the quantised token rows, [M][K/2] and [M][K/16]
+ *   b_codes/b_scales  the weight, [N][K/2] and [N][K/16]
+ *   alpha_b           device float32: the weight's tensor scale, or
+ *   alpha_b_rows      nullable device float32 [N]: the tensor scale of each
+ *                     B row (stacked weights as in w4a4_gemm_multi); when
+ *                     set it is used instead of alpha_b.
+ * M must lie in [0, NVFP4_DECODE_MAX_ROWS] (else NVFP4_ERR_SHAPE); larger
+ * batches go to w4a4_gemm.  Scales need 2-byte alignment when K % 32 == 0.
+ * Outputs are within the same bound of the exact product as w4a4_gemm's
+ * (float32 sums in another order, so not bit-identical to it).  Ownership,
+ * stream and other errors as for w4a4_gemm.
+ */
+#define NVFP4_DECODE_MAX_ROWS 64
+nvfp4_status_t w4a4_gemm_decode(const uint8_t* a_codes, const uint8_t* a_scales,
+                                const float* alpha_a, const uint8_t* b_codes,
+                                const uint8_t* b_scales, const float* alpha_b,
+                                const float* alpha_b_rows, int64_t M, int64_t N, int64_t K,
+                                float* y_f32, uint16_t* y_bf16, int64_t ld_y,
+                                hipStream_t stream);
+
+/*
  * w4a4_gemm_grouped - the W4A4 GEMM of a mixture-of-experts layer: one
  * launch over num_groups experts with ragged row counts.
  *

@@ -32,6 +32,8 @@ _SIGNATURES = {
                   _c_i64, _c_void, _c_void, _c_i64, _c_void],
     "w4a4_gemm_multi": [_c_void, _c_void, _c_void, _c_void, _c_void, _c_void, _c_i64, _c_i64,
                         _c_i64, _c_void, _c_void, _c_i64, _c_void],
+    "w4a4_gemm_decode": [_c_void, _c_void, _c_void, _c_void, _c_void, _c_void, _c_void,
+                         _c_i64, _c_i64, _c_i64, _c_void, _c_void, _c_i64, _c_void],
     "w4a4_gemm_grouped": [_c_void, _c_void, _c_void, _c_i64, _c_void, _c_void, _c_void,
                           _c_void, _c_i64, _c_i64, _c_i64, _c_i32, _c_void, _c_void,
                           _c_void, _c_i64, _c_void],
@@ -235,6 +237,27 @@ def w4a4_gemm_multi(a: NVFP4Tensor, b: NVFP4Stack, f32: bool = True, bf16: bool 
     ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
     _call("w4a4_gemm_multi", _ptr(a.codes), _ptr(a.scales), _ptr(a.alpha), _ptr(b.codes),
           _ptr(b.scales), _ptr(b.alpha_rows), m, n, k, _ptr(y_f32), _ptr(y_bf16), ld,
+          _stream(a.codes.device))
+    return y_f32, y_bf16
+
+
+DECODE_MAX_ROWS = 64
+
+
+def w4a4_gemm_decode(a: NVFP4Tensor, b, f32: bool = True, bf16: bool = True,
+                     y_f32: torch.Tensor | None = None, y_bf16: torch.Tensor | None = None):
+    """Decode-shaped W4A4 GEMM (a.rows <= DECODE_MAX_ROWS) against an
+    NVFP4Tensor weight or an NVFP4Stack (per-row tensor scales)."""
+    m, k = a.rows, a.k
+    n = b.rows
+    if b.k != k:
+        raise ValueError("operands disagree on K")
+    y_f32, y_bf16 = _outputs(m, n, a.codes.device, f32, bf16, y_f32, y_bf16)
+    ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
+    stacked = isinstance(b, NVFP4Stack)
+    _call("w4a4_gemm_decode", _ptr(a.codes), _ptr(a.scales), _ptr(a.alpha), _ptr(b.codes),
+          _ptr(b.scales), None if stacked else _ptr(b.alpha),
+          _ptr(b.alpha_rows) if stacked else None, m, n, k, _ptr(y_f32), _ptr(y_bf16), ld,
           _stream(a.codes.device))
     return y_f32, y_bf16
 

@@ -226,6 +226,42 @@ nvfp4_status_t w4a4_gemm_multi(const uint8_t* a_codes, const uint8_t* a_scales,
                      alpha_b_rows, M, N, K, 1, nullptr, y_f32, y_bf16, ld_y, stream);
 }
 
+nvfp4_status_t w4a4_gemm_decode(const uint8_t* a_codes, const uint8_t* a_scales,
+                                const float* alpha_a, const uint8_t* b_codes,
+                                const uint8_t* b_scales, const float* alpha_b,
+                                const float* alpha_b_rows, int64_t M, int64_t N, int64_t K,
+                                float* y_f32, uint16_t* y_bf16, int64_t ld_y,
+                                hipStream_t stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 16 != 0 || M > NVFP4_DECODE_MAX_ROWS || N >= kMaxDim ||
+      K >= kMaxDim)
+    return NVFP4_ERR_SHAPE;
+  nvfp4_status_t st = check_outputs(y_f32, y_bf16, N, ld_y);
+  if (st != NVFP4_OK) return st;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!a_codes || !a_scales || !alpha_a || !b_codes || !b_scales || !(alpha_b || alpha_b_rows))
+    return NVFP4_ERR_NULL;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16)) return NVFP4_ERR_ALIGN;
+  if (K % 32 == 0 && (!aligned(a_scales, 2) || !aligned(b_scales, 2))) return NVFP4_ERR_ALIGN;
+  // the kernel addresses each operand with 32-bit byte offsets
+  if (N * (K / 2) > (int64_t(1) << 32) - 1) return NVFP4_ERR_SHAPE;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  nvfp4::DecodeArgs a;
+  a.a_codes = a_codes;
+  a.a_scales = a_scales;
+  a.alpha_a = alpha_a;
+  a.b_codes = b_codes;
+  a.b_scales = b_scales;
+  a.alpha_b = alpha_b;
+  a.alpha_b_rows = alpha_b_rows;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.y_f32 = y_f32;
+  a.y_bf16 = y_bf16;
+  a.ld_y = ld_y;
+  return launched(nvfp4::launch_w4a4_decode(a, stream));
+}
+
 nvfp4_status_t w4a4_gemm_grouped(const uint8_t* a_codes, const uint8_t* a_scales,
                                  const float* alpha_a, int64_t a_rows,
                                  const int32_t* a_row_index, const uint8_t* b_codes,

@@ -1,0 +1,504 @@
+// Decode-shaped NVFP4 W4A4 GEMM for gfx950: a few token rows (M <= 64)
+// against a whole weight matrix, the shape of the decode steps in the
+// uniform-NVFP4 configuration that Mix-Quant is compared with
+// ("Mix-Quant：面向智能体LLM的量化预填充与精确解码", paper.rainbus.top digest,
+// 实验结果, Table 1 and the phase-wise ablation of Table 3).  The arithmetic
+// is the W4A4 linear layer of the same digest (核心方法; 方法步骤详情 steps (3)
+// and (4)):
+//
+//   Y[m][n] = alpha_a alpha_b sum_b sigma^a_{m,b} sigma^b_{n,b}
+//             sum_{k in b} q^a_{m,k} q^b_{n,k}
+//
+// At this shape the work is a stream over the weight codes (0.5625 bytes a
+// weight): the kernel is bound by HBM, not by the matrix cores.  Layout:
+//
+//  - A workgroup (4 waves) owns 16 output columns and all of K.  The K axis
+//    is cut into 32-element chunks (16 code bytes and 2 scale bytes a row);
+//    the 16 lane groups of the workgroup (wave w, lane group g = lane / 16)
+//    take chunks 4w + g, 4w + g + 16, ... so that each row is read in runs
+//    of 256 contiguous code bytes.  Lane l of a group reads chunk data of
+//    weight row n0 + l % 16 and of token row l % 16 (+ 16 t for M-tile t).
+//  - Both operands are decoded to float16 with the block scale folded in
+//    (exact: every q * sigma has at most 6 significant bits) and multiplied
+//    by v_mfma_f32_16x16x32_f16, whose operand lanes hold 8 K-elements of
+//    one row (lane group g supplies K-slots 8g..8g+7).  A and B lanes of one
+//    group supply the same chunk, so the contraction pairs the right
+//    elements; which chunk lands in which K-slot does not matter to a sum.
+//  - The four waves' float32 partial sums meet in LDS and are added in a
+//    fixed order (wave 0 + 1 + 2 + 3), then scaled by alpha_a alpha_b 2^8.
+#include "device_common.h"
+#include "kernels.h"
+
+#include <cstdlib>
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kCols = 16;                 // output columns per workgroup
+constexpr int kGroups = kWaves * 4;       // lane groups sharing a row's chunks
+constexpr int kDepth = 4;                 // chunks in flight per lane
+
+// s_waitcnt immediate (gfx9 encoding): vector-memory count n, no expcnt
+// wait, LDS/scalar count 0.
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// sigma (E4M3FN byte) -> float16 sigma * 2^-8 in both halves (the byte's
+// exponent and mantissa fields land in the f16 fields; a subnormal E4M3
+// byte becomes a subnormal f16).
+__device__ __forceinline__ half2_t scale_pair(uint32_t sb) {
+  return __builtin_bit_cast(half2_t, sb * 0x00800080u);
+}
+
+// 8 FP4 codes (one 32-bit word, element 2j in the low nibble of byte j) ->
+// 8 float16 values q * sigma * 2^-4, exactly: the conversion multiplies by
+// 16 (the exponent of its scale operand), the packed multiply by sigma 2^-8.
+__device__ __forceinline__ half8_t decode8(uint32_t w, half2_t s) {
+  half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 16.0f, 0) * s;
+  half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 16.0f, 1) * s;
+  half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 16.0f, 2) * s;
+  half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 16.0f, 3) * s;
+  half8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// The codes (16 bytes) and the two scale bytes of one row's 32-element chunk
+// j, loaded from a clamped (always valid) chunk index: the loads are
+// unconditional, so the compiler keeps them in flight across the pipeline.
+// A chunk past the end of the row, or a token row that is not there, is
+// removed where the data is used, by a zero A scale (a zero scale decodes
+// to zero whatever the codes; B never needs it, since every B value meets an
+// A value).  kFull: K % 32 == 0, so a chunk is whole and its scale pair is
+// 2-byte aligned.  Otherwise the last chunk holds one block (16 elements),
+// whose second half repeats the first and gets a zero A scale.  kStream:
+// the data is read once (non-temporal loads).
+struct ChunkData {
+  u32x4 codes;
+  uint32_t scales;     // byte 0: block 2j, byte 1: block 2j + 1
+};
+
+// Raw buffer resource (stride 0, plain 32-bit data format) over
+// [base, base + bytes).  Buffer loads are intrinsics, not plain loads, so
+// the compiler does not move them next to their use in a later iteration.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// codes_off / scales_off: byte offsets of the row in the two buffers.
+template <bool kFull, bool kStream>
+__device__ __forceinline__ ChunkData load_chunk(__amdgpu_buffer_rsrc_t rc, uint32_t codes_off,
+                                                __amdgpu_buffer_rsrc_t rs, uint32_t scales_off,
+                                                int j, int n_chunks, int n_blocks) {
+  constexpr int kPolicy = kStream ? 2 : 0;          // nt: read once
+  const uint32_t jc = (uint32_t)(j < n_chunks ? j : n_chunks - 1);
+  ChunkData d;
+  if (kFull) {
+    d.codes = __builtin_amdgcn_raw_buffer_load_b128(rc, codes_off + 16u * jc, 0, kPolicy);
+    d.scales = __builtin_amdgcn_raw_buffer_load_b16(rs, scales_off + 2u * jc, 0, 0);
+  } else {
+    const uint32_t second = 2 * jc + 1 < (uint32_t)n_blocks ? 1u : 0u;  // the chunk is whole
+    const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(rc, codes_off + 16u * jc, 0, kPolicy);
+    const u32x2 hi =
+        __builtin_amdgcn_raw_buffer_load_b64(rc, codes_off + 16u * jc + 8u * second, 0, kPolicy);
+    d.codes = u32x4{lo.x, lo.y, hi.x, hi.y};
+    d.scales = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, scales_off + 2u * jc, 0, 0) |
+               ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, scales_off + 2u * jc + second,
+                                                              0, 0) << 8);
+  }
+  return d;
+}
+
+// Which scale bytes of chunk j are real (0xFFFF, 0x00FF for a half chunk,
+// 0 past the end).
+__device__ __forceinline__ uint32_t chunk_mask(int j, int n_chunks, int n_blocks) {
+  if (j >= n_chunks) return 0u;
+  return 2 * j + 1 < n_blocks ? 0xFFFFu : 0x00FFu;
+}
+
+template <int MT, bool kFull>
+__global__ __launch_bounds__(kThreads) void w4a4_decode_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const float* __restrict__ alpha_a, const uint8_t* __restrict__ b_codes,
+    const uint8_t* __restrict__ b_scales, const float* __restrict__ alpha_b,
+    const float* __restrict__ alpha_b_rows, int M, int N, int K,
+    float* __restrict__ y_f32, uint16_t* __restrict__ y_bf16, int64_t ld_y) {
+  __shared__ float red[kWaves][MT][16][17];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int group = wave * 4 + (lane >> 4);
+  const int n0 = blockIdx.x * kCols;
+  const int n_chunks = (K + 31) / 32;
+  const int n_blocks = K / 16;
+  const int64_t row_codes = K / 2, row_scales = K / 16;
+
+  const int nb = n0 + r16 < N ? n0 + r16 : N - 1;
+  const __amdgpu_buffer_rsrc_t rbc = buffer_of(b_codes, (uint32_t)(N * row_codes));
+  const __amdgpu_buffer_rsrc_t rbs = buffer_of(b_scales, (uint32_t)(N * row_scales));
+  const __amdgpu_buffer_rsrc_t rac = buffer_of(a_codes, (uint32_t)(M * row_codes));
+  const __amdgpu_buffer_rsrc_t ras = buffer_of(a_scales, (uint32_t)(M * row_scales));
+  const uint32_t bc = (uint32_t)(nb * row_codes), bs = (uint32_t)(nb * row_scales);
+  uint32_t ac[MT], as[MT];
+  bool a_ok[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = 16 * t + r16;
+    a_ok[t] = m < M;
+    const int mc = a_ok[t] ? m : 0;
+    ac[t] = (uint32_t)(mc * row_codes);
+    as[t] = (uint32_t)(mc * row_scales);
+  }
+
+  float4_t acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // chunks of this lane: group, group + 16, ...  The trip count is that of
+  // the workgroup's first lane group rounded up to whole pipeline rounds, so
+  // the loop body has no branch (which would make the compiler drain the
+  // loads in flight) and all lanes of a wave run the MFMAs together; a lane
+  // whose chunk is past the end supplies zeros.
+  const int iters = (n_chunks + kGroups - 1) / kGroups;
+
+  ChunkData b_buf[kDepth];
+  ChunkData a_buf[kDepth][MT];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    const int j = group + kGroups * d;
+    b_buf[d] = load_chunk<kFull, true>(rbc, bc, rbs, bs, j, n_chunks, n_blocks);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      a_buf[d][t] = load_chunk<kFull, false>(rac, ac[t], ras, as[t], j, n_chunks, n_blocks);
+  }
+
+  for (int i0 = 0; i0 < iters; i0 += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      {
+        // decode the chunk in hand first, so that its raw registers are free
+        // for the refill; the refill is then in flight during the MFMAs
+        const int jd = group + kGroups * (i0 + d);
+        const uint32_t mask = chunk_mask(jd, n_chunks, n_blocks);
+        const uint32_t bw[4] = {b_buf[d].codes.x, b_buf[d].codes.y, b_buf[d].codes.z,
+                                b_buf[d].codes.w};
+        half8_t bv[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          bv[s] = decode8(bw[s], scale_pair((b_buf[d].scales >> (8 * (s >> 1))) & 0xFFu));
+        half8_t av[MT][4];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const uint32_t aw[4] = {a_buf[d][t].codes.x, a_buf[d][t].codes.y,
+                                  a_buf[d][t].codes.z, a_buf[d][t].codes.w};
+          const uint32_t as_eff = a_ok[t] ? (a_buf[d][t].scales & mask) : 0u;
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            av[t][s] = decode8(aw[s], scale_pair((as_eff >> (8 * (s >> 1))) & 0xFFu));
+        }
+        // refill this slot with the chunk kDepth iterations ahead
+        const int j = jd + kGroups * kDepth;
+        b_buf[d] = load_chunk<kFull, true>(rbc, bc, rbs, bs, j, n_chunks, n_blocks);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          a_buf[d][t] = load_chunk<kFull, false>(rac, ac[t], ras, as[t], j, n_chunks, n_blocks);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t][s], bv[s], acc[t], 0, 0, 0);
+      }
+    }
+  }
+
+  // D layout of the 16x16 MFMA: lane l holds rows 4 (l / 16) + r, column l % 16
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][t][4 * (lane >> 4) + r][r16] = acc[t][r];
+  __syncthreads();
+
+  const int n = threadIdx.x & 15;
+  const int col = n0 + n;
+  if (col >= N) return;
+  const float ab = alpha_b_rows != nullptr ? alpha_b_rows[col] : *alpha_b;
+  const float scale = (*alpha_a) * ab * 256.0f;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int mr = threadIdx.x >> 4;          // 0..15
+    const int m = 16 * t + mr;
+    if (m >= M) continue;
+    float v = red[0][t][mr][n];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) v += red[w][t][mr][n];
+    v *= scale;
+    if (y_f32 != nullptr) y_f32[m * ld_y + col] = v;
+    if (y_bf16 != nullptr) y_bf16[m * ld_y + col] = (uint16_t)f32_to_bf16_bits(v);
+  }
+}
+
+// ---- LDS-staged variant (K % 64 == 0) --------------------------------------
+// The stream over B is what the kernel waits for, and HBM serves it best in
+// long runs of one row.  Here each K-stage (512 elements: 256 code bytes and
+// 32 scale bytes a row) of the workgroup's 16 B rows, and of the 16 * MT
+// token rows, goes global -> LDS by buffer_load ... lds: one wave
+// instruction moves 4 rows x 256 contiguous bytes.  Lane i of the
+// instruction fetches chunk (i % 16) ^ (row & 15) of its row into slot
+// i % 16, so that the MFMA-layout reads (16 rows, one chunk) hit 16 distinct
+// bank groups.  A ring of S stages keeps S - 1 stages in flight; past the
+// last stage the loads repeat the last stage into the slot being refilled,
+// which nobody reads again, so the wait count stays constant.  Each lane
+// then handles one 32-element chunk of a stage (chunk 4 * wave + lane / 16).
+constexpr int kStageCodes = 256;                       // code bytes a row and stage
+constexpr int kStageScales = 32;                       // scale bytes a row and stage
+constexpr int kTileBytes = 16 * (kStageCodes + kStageScales);   // 4608
+
+__device__ __forceinline__ void dma16_lds(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4_lds(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 4,
+                                           voff, 0, 0, 0);
+}
+
+// A workgroup takes at most kMaxTiles column tiles (blockIdx.x,
+// blockIdx.x + gridDim.x, ...), streams all of them through the ring without
+// a break, and keeps one accumulator set per tile; the cross-wave sums come
+// at the very end.  (An LDS write while loads into LDS are in flight makes
+// the compiler wait for them, which would drain the ring at every tile.)
+constexpr int kMaxTiles = 8;
+
+template <int MT, int S>
+__global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const float* __restrict__ alpha_a, const uint8_t* __restrict__ b_codes,
+    const uint8_t* __restrict__ b_scales, const float* __restrict__ alpha_b,
+    const float* __restrict__ alpha_b_rows, int M, int N, int K,
+    float* __restrict__ y_f32, uint16_t* __restrict__ y_bf16, int64_t ld_y) {
+  constexpr int kTiles = 1 + MT;                       // B tile, then the A tiles
+  // scale DMAs: 8 rows x 32 bytes of one tile each (all 64 lanes); wave w
+  // takes halves w, w + 4, ...; a wave left without one reloads a valid
+  // half into a slack area, so every wave counts the same loads
+  constexpr int kScaleDmas = (2 * kTiles + kWaves - 1) / kWaves;
+  constexpr int kStage = kTiles * kTileBytes + 256;    // + slack
+  constexpr int kRed = kWaves * MT * 16 * 17 * 4;      // one tile's partial sums
+  static_assert(kRed <= S * kStage, "the reduction fits in the ring");
+  __shared__ __align__(16) uint8_t lds[S * kStage];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15;
+  const int n_chunks = K / 32;
+  const int n_stages = (K / 2 + kStageCodes - 1) / kStageCodes;
+  const int64_t row_codes = K / 2, row_scales = K / 16;
+  const int n_tiles = (N + kCols - 1) / kCols;
+  const int my_tiles = (n_tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int total = my_tiles * n_stages;               // stages this workgroup computes
+
+  const __amdgpu_buffer_rsrc_t rbc = buffer_of(b_codes, (uint32_t)(N * row_codes));
+  const __amdgpu_buffer_rsrc_t rbs = buffer_of(b_scales, (uint32_t)(N * row_scales));
+  const __amdgpu_buffer_rsrc_t rac = buffer_of(a_codes, (uint32_t)(M * row_codes));
+  const __amdgpu_buffer_rsrc_t ras = buffer_of(a_scales, (uint32_t)(M * row_scales));
+
+  // DMA lane offsets at stage 0.  Codes, per tile: row 4 * wave + lane / 16,
+  // slot lane % 16 (1 KB a wave).  Scales, per half h of a tile: row
+  // 8 h + lane / 8, bytes 4 (lane % 8) .. + 3 (K % 64 == 0 keeps them 4-byte
+  // aligned).  B rows past N repeat row N - 1 (their outputs are dropped);
+  // token rows past M repeat row M - 1 (their A scales are zeroed).
+  const int dma_row = 4 * wave + (lane >> 4);
+  const int dma_chunk = r16 ^ dma_row;                 // dma_row < 16
+  auto a_row = [&](int t, int r) { return 16 * t + r < M ? 16 * t + r : M - 1; };
+  uint32_t a_code_off[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+    a_code_off[t] = (uint32_t)(a_row(t, dma_row) * row_codes) + 16u * dma_chunk;
+  int sc_tile[kScaleDmas], sc_r[kScaleDmas];
+  uint32_t a_scale_off[kScaleDmas];
+#pragma unroll
+  for (int d = 0; d < kScaleDmas; ++d) {
+    const int half = d * kWaves + wave;                // uniform
+    const int hh = half < 2 * kTiles ? half : 0;
+    sc_tile[d] = hh >> 1;
+    sc_r[d] = 8 * (hh & 1) + (lane >> 3);
+    a_scale_off[d] = sc_tile[d] == 0 ? 0u
+                     : (uint32_t)(a_row(sc_tile[d] - 1, sc_r[d]) * row_scales) + 4u * (lane & 7);
+  }
+  // global stage g -> (column tile, stage within the tile); past the end
+  // the last stage is loaded again (into a slot nobody reads any more)
+  auto issue = [&](int g) __attribute__((always_inline)) {
+    const int gc = g < total ? g : total - 1;
+    const int tile = (int)blockIdx.x + (gc / n_stages) * (int)gridDim.x;
+    const uint32_t st = (uint32_t)(gc % n_stages);
+    const int nb0 = tile * kCols;
+    uint8_t* base = lds + (g % S) * kStage;
+    const int rb = nb0 + dma_row < N ? nb0 + dma_row : N - 1;
+    dma16_lds(rbc, base + wave * 1024,
+              (uint32_t)(rb * row_codes) + 16u * dma_chunk + st * kStageCodes);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      dma16_lds(rac, base + (1 + t) * kTileBytes + wave * 1024, a_code_off[t] + st * kStageCodes);
+#pragma unroll
+    for (int d = 0; d < kScaleDmas; ++d) {
+      const int half = d * kWaves + wave;
+      uint8_t* dst = half < 2 * kTiles
+                         ? base + (half >> 1) * kTileBytes + 16 * kStageCodes + (half & 1) * 256
+                         : base + kTiles * kTileBytes;
+      // branch-free (a branch here makes the compiler drain the loads)
+      const bool is_b = sc_tile[d] == 0;
+      const int rs = nb0 + sc_r[d] < N ? nb0 + sc_r[d] : N - 1;
+      const uint32_t off = is_b ? (uint32_t)(rs * row_scales) + 4u * (lane & 7) : a_scale_off[d];
+      dma4_lds(is_b ? rbs : ras, dst, off + st * kStageScales);
+    }
+  };
+  constexpr int kDmaPerStage = kTiles + kScaleDmas;
+
+  float4_t acc[kMaxTiles][MT];
+#pragma unroll
+  for (int tt = 0; tt < kMaxTiles; ++tt)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[tt][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+  bool a_ok[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) a_ok[t] = 16 * t + r16 < M;
+  const int q = 4 * wave + (lane >> 4);                 // this lane's chunk of a stage
+  const int rd_code = r16 * kStageCodes + ((q ^ r16) << 4);
+  const int rd_scale = 16 * kStageCodes + r16 * kStageScales + 2 * q;
+
+#pragma unroll
+  for (int g = 0; g < S - 1; ++g) issue(g);
+
+  int g = 0;
+#pragma unroll
+  for (int tt = 0; tt < kMaxTiles; ++tt) {
+    if (tt < my_tiles) {
+      for (int st = 0; st < n_stages; ++st, ++g) {
+        // this wave's loads of stage g are done when at most S - 2 stages of
+        // loads are younger; the barrier makes every wave's part visible
+        // and frees the slot of stage g - 1 for the refill (a bare
+        // s_barrier: __syncthreads would also wait for every load in
+        // flight; the stage's LDS reads cannot move above it, since the
+        // refill loads, which write LDS, are issued between the two)
+        __builtin_amdgcn_s_waitcnt(vm_wait((S - 2) * kDmaPerStage));
+        __builtin_amdgcn_s_barrier();
+        issue(g + S - 1);
+        const uint8_t* base = lds + (g % S) * kStage;
+        const uint32_t mask = st * 16 + q < n_chunks ? 0xFFFFu : 0u;
+        const u32x4 bc = *reinterpret_cast<const u32x4*>(base + rd_code);
+        const uint32_t bs = *reinterpret_cast<const uint16_t*>(base + rd_scale);
+        u32x4 ac[MT];
+        uint32_t as[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const uint8_t* tl = base + (1 + t) * kTileBytes;
+          ac[t] = *reinterpret_cast<const u32x4*>(tl + rd_code);
+          as[t] = *reinterpret_cast<const uint16_t*>(tl + rd_scale) & (a_ok[t] ? mask : 0u);
+        }
+        const uint32_t bw[4] = {bc.x, bc.y, bc.z, bc.w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const half8_t bv = decode8(bw[s], scale_pair((bs >> (8 * (s >> 1))) & 0xFFu));
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const uint32_t aw = s == 0 ? ac[t].x : s == 1 ? ac[t].y : s == 2 ? ac[t].z : ac[t].w;
+            const half8_t av = decode8(aw, scale_pair((as[t] >> (8 * (s >> 1))) & 0xFFu));
+            acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[tt][t], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // every tile's four wave partials meet in LDS (the ring, once no load is
+  // still writing it); D layout of the 16x16 MFMA: lane l holds rows
+  // 4 (l / 16) + r, column l % 16
+  __builtin_amdgcn_s_waitcnt(vm_wait(0));
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);          // [wave][t][16][17]
+  const float alpha_x = *alpha_a;
+  const int n = threadIdx.x & 15, mr = threadIdx.x >> 4;
+#pragma unroll
+  for (int tt = 0; tt < kMaxTiles; ++tt) {
+    if (tt < my_tiles) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          red[((wave * MT + t) * 16 + 4 * (lane >> 4) + r) * 17 + r16] = acc[tt][t][r];
+      __syncthreads();
+      const int col = ((int)blockIdx.x + tt * (int)gridDim.x) * kCols + n;
+      if (col < N) {
+        const float ab = alpha_b_rows != nullptr ? alpha_b_rows[col] : *alpha_b;
+        const float scale = alpha_x * ab * 256.0f;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int m = 16 * t + mr;
+          if (m < M) {
+            float v = red[((0 * MT + t) * 16 + mr) * 17 + n];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) v += red[((w * MT + t) * 16 + mr) * 17 + n];
+            v *= scale;
+            if (y_f32 != nullptr) y_f32[m * ld_y + col] = v;
+            if (y_bf16 != nullptr) y_bf16[m * ld_y + col] = (uint16_t)f32_to_bf16_bits(v);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+template <int MT>
+hipError_t launch_mt(const DecodeArgs& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((p.N + kCols - 1) / kCols));
+  constexpr int kS = MT == 1 ? 8 : MT == 2 ? 5 : 3;
+  if (p.K % 64 == 0 && std::getenv("NVFP4_DECODE_DIRECT") == nullptr) {
+    // persistent workgroups: as many as fit on the chip at once, at most
+    // one per column tile
+    static int per_cu_cache[64];
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    int& per_cu = per_cu_cache[dev & 63];
+    if (per_cu == 0) {
+      int occ = 0, cus = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, w4a4_decode_lds_kernel<MT, kS>,
+                                                       kThreads, 0) != hipSuccess || occ < 1)
+        occ = 1;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          cus < 1)
+        cus = 256;
+      per_cu = occ * cus;
+    }
+    // as many workgroups as fit at once, at most one per column tile, and
+    // enough that none takes more than kMaxTiles tiles
+    const int tiles = (int)((p.N + kCols - 1) / kCols);
+    int wgs = tiles < per_cu ? tiles : per_cu;
+    const int need = (tiles + kMaxTiles - 1) / kMaxTiles;
+    if (wgs < need) wgs = need;
+    const dim3 pgrid((unsigned)wgs);
+    hipLaunchKernelGGL((w4a4_decode_lds_kernel<MT, kS>), pgrid, dim3(kThreads), 0, stream,
+                       p.a_codes, p.a_scales, p.alpha_a, p.b_codes, p.b_scales, p.alpha_b,
+                       p.alpha_b_rows, (int)p.M, (int)p.N, (int)p.K, p.y_f32, p.y_bf16, p.ld_y);
+  } else if (p.K % 32 == 0)
+    hipLaunchKernelGGL((w4a4_decode_kernel<MT, true>), grid, dim3(kThreads), 0, stream,
+                       p.a_codes, p.a_scales, p.alpha_a, p.b_codes, p.b_scales, p.alpha_b,
+                       p.alpha_b_rows, (int)p.M, (int)p.N, (int)p.K, p.y_f32, p.y_bf16, p.ld_y);
+  else
+    hipLaunchKernelGGL((w4a4_decode_kernel<MT, false>), grid, dim3(kThreads), 0, stream,
+                       p.a_codes, p.a_scales, p.alpha_a, p.b_codes, p.b_scales, p.alpha_b,
+                       p.alpha_b_rows, (int)p.M, (int)p.N, (int)p.K, p.y_f32, p.y_bf16, p.ld_y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_w4a4_decode(const DecodeArgs& p, hipStream_t stream) {
+  if (p.M <= 16) return launch_mt<1>(p, stream);
+  if (p.M <= 32) return launch_mt<2>(p, stream);
+  return launch_mt<4>(p, stream);
+}
+
+}  // namespace nvfp4

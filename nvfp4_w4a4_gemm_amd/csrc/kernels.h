@@ -75,6 +75,22 @@ struct W4A4Args {
 hipError_t launch_w4a4(const W4A4Args& args, hipStream_t stream);
 hipError_t launch_w4a4_fused(const W4A4Args& args, hipStream_t stream);
 
+// Decode-shaped W4A4 GEMM (M <= 64): codes/scales/alphas as in W4A4Args.
+struct DecodeArgs {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const float* alpha_a;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  const float* alpha_b;           // used when alpha_b_rows is null
+  const float* alpha_b_rows;      // nullable: tensor scale of each B row [N]
+  int64_t M, N, K;
+  float* y_f32;
+  uint16_t* y_bf16;
+  int64_t ld_y;
+};
+hipError_t launch_w4a4_decode(const DecodeArgs& args, hipStream_t stream);
+
 struct Bf16Args {
   const uint16_t* x;
   const uint16_t* w;

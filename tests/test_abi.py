@@ -33,7 +33,8 @@ def header_functions():
 def test_header_declares_the_four_entry_points():
     names = header_functions()
     for n in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "w4a4_gemm", "bf16_gemm_baseline",
-              "w4a4_gemm_multi", "w4a4_gemm_grouped", "w4a4_gemm_fused_act"):
+              "w4a4_gemm_multi", "w4a4_gemm_grouped", "w4a4_gemm_fused_act",
+              "w4a4_gemm_decode"):
         assert n in names
 
 
@@ -137,6 +138,35 @@ def test_gemm_multi_validation(lib):
     assert f(*bad) == SHAPE
     bad = list(args); bad[3] = p(4)
     assert f(*bad) == ALIGN
+
+
+@needs_lib
+def test_gemm_decode_validation(lib):
+    f = lib.w4a4_gemm_decode
+    # a_codes, a_scales, alpha_a, b_codes, b_scales, alpha_b, alpha_b_rows, M, N, K,
+    # y32, y16, ld, stream
+    args = [p(), p(), p(), p(), p(), p(), None, 16, 96, 256, p(), p(), 96, None]
+    assert f(*args) == UNSUPPORTED
+    rows = list(args); rows[5] = None; rows[6] = p()          # per-row scales instead
+    assert f(*rows) == UNSUPPORTED
+    bad = list(args); bad[5] = None                           # neither tensor scale
+    assert f(*bad) == NULL
+    bad = list(args); bad[7] = 65                             # more rows than decode takes
+    assert f(*bad) == SHAPE
+    ok64 = list(args); ok64[7] = 64
+    assert f(*ok64) == UNSUPPORTED
+    bad = list(args); bad[9] = 40
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[4] = p(1)                           # scale pairs are 2-byte loads
+    assert f(*bad) == ALIGN
+    odd = list(args); odd[9] = 272; odd[4] = p(1)             # K % 32 != 0: byte loads
+    assert f(*odd) == UNSUPPORTED
+    bad = list(args); bad[3] = p(8)
+    assert f(*bad) == ALIGN
+    bad = list(args); bad[8] = 1 << 22; bad[9] = 1 << 11; bad[12] = 1 << 22  # > 4 GiB of B
+    assert f(*bad) == SHAPE
+    zero = list(args); zero[7] = 0
+    assert f(*zero) == OK
 
 
 @needs_lib

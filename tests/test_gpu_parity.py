@@ -251,6 +251,82 @@ def test_w4a4_gemm_deterministic():
     assert torch.equal(a1, a2) and torch.equal(b1.view(torch.int16), b2.view(torch.int16))
 
 
+@pytest.mark.parametrize("m,n,k", [(1, 1024, 1024), (16, 200, 1408), (5, 50, 48),
+                                   (64, 300, 256), (33, 17, 2816), (17, 1, 16),
+                                   (1, 4096, 4096), (3, 129, 4112), (48, 96, 544)])
+def test_w4a4_gemm_decode_matches_oracle(m, n, k):
+    """Decode shape (M <= 64): one, two and four 16-row tiles, K with a
+    half chunk at the end (K % 32 == 16), a single column, ragged N."""
+    xb, wb = quantized_pair(m, n, k, seed=3 * m + n + k)
+    qa = nv.nvfp4_quantize_act(dev_bf16(xb))
+    qw = nv.nvfp4_quantize_weights(dev_bf16(wb))
+    y32, y16 = nv.w4a4_gemm_decode(qa, qw)
+    y, bound, y16_ref = orc.w4a4_reference(orc.quantize(xb), orc.quantize(wb))
+    assert_gemm_close(y32, y16, y, bound, y16_ref)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (20, 64, 2816), (64, 33, 512)])
+def test_w4a4_gemm_decode_direct_path(monkeypatch, m, n, k):
+    """The register-load decode kernel (taken when K % 64 != 0) on shapes the
+    LDS-staged one would take, forced by NVFP4_DECODE_DIRECT: both agree with
+    the oracle."""
+    xb, wb = quantized_pair(m, n, k, seed=5 * m + n + k)
+    qa = nv.nvfp4_quantize_act(dev_bf16(xb))
+    qw = nv.nvfp4_quantize_weights(dev_bf16(wb))
+    y, bound, y16_ref = orc.w4a4_reference(orc.quantize(xb), orc.quantize(wb))
+    s32, s16 = nv.w4a4_gemm_decode(qa, qw)
+    monkeypatch.setenv("NVFP4_DECODE_DIRECT", "1")
+    d32, d16 = nv.w4a4_gemm_decode(qa, qw)
+    assert_gemm_close(s32, s16, y, bound, y16_ref)
+    assert_gemm_close(d32, d16, y, bound, y16_ref)
+
+
+def test_w4a4_gemm_decode_subnormal_scales_and_stacked_weights():
+    """Subnormal block scales in both operands, and weights stacked along N
+    under three tensor scales (per-row alpha)."""
+    m, k = 12, 512
+    rng = np.random.default_rng(78)
+    x = (rng.standard_normal((m, k)) * 0.01).astype(np.float32)
+    x[0, 5] = 1000.0
+    xb = bf16_bits(x)
+    ra = orc.quantize(xb)
+    assert (orc.e4m3_decode(ra[1][1:]) < 2.0 ** -6).mean() > 0.9
+    parts = []
+    for i, (n, std) in enumerate(((64, 0.0002), (40, 0.5), (30, 3.0))):
+        w = (rng.standard_normal((n, k)) * std).astype(np.float32)
+        w[1, 9] = 50.0 * std * 1e4 if i == 0 else w[1, 9]
+        parts.append(bf16_bits(w))
+    qa = nv.nvfp4_quantize_act(dev_bf16(xb))
+    qws = [nv.nvfp4_quantize_weights(dev_bf16(w)) for w in parts]
+    stack = nv.stack_tensors(qws)
+    y32, y16 = nv.w4a4_gemm_decode(qa, stack)
+    for q, w, lo, hi in zip(qws, parts, stack.offsets[:-1], stack.offsets[1:]):
+        y, bound, y16_ref = orc.w4a4_reference(ra, orc.quantize(w))
+        assert_gemm_close(y32[:, lo:hi], y16[:, lo:hi], y, bound, y16_ref)
+        s32, _ = nv.w4a4_gemm_decode(qa, q)
+        assert torch.equal(y32[:, lo:hi], s32)
+
+
+def test_w4a4_gemm_decode_output_modes():
+    """float32 only, BF16 only, and a leading dimension wider than N: the
+    columns past N are left alone; repeated calls are bit-identical."""
+    m, n, k = 7, 90, 640
+    xb, wb = quantized_pair(m, n, k, seed=91)
+    qa = nv.nvfp4_quantize_act(dev_bf16(xb))
+    qw = nv.nvfp4_quantize_weights(dev_bf16(wb))
+    y, bound, y16_ref = orc.w4a4_reference(orc.quantize(xb), orc.quantize(wb))
+    y32 = torch.full((m, n + 13), 7.0, device=DEV)
+    y16 = torch.full((m, n + 13), 7.0, device=DEV, dtype=torch.bfloat16)
+    nv.w4a4_gemm_decode(qa, qw, y_f32=y32[:, :n], bf16=False)
+    nv.w4a4_gemm_decode(qa, qw, f32=False, y_bf16=y16[:, :n])
+    assert_gemm_close(y32[:, :n], y16[:, :n], y, bound, y16_ref)
+    assert torch.all(y32[:, n:] == 7.0) and torch.all(y16[:, n:] == 7.0)
+    a32, a16 = nv.w4a4_gemm_decode(qa, qw)
+    b32, b16 = nv.w4a4_gemm_decode(qa, qw)
+    assert torch.equal(a32, b32) and torch.equal(a16.view(torch.int16), b16.view(torch.int16))
+    assert torch.equal(a32, y32[:, :n])
+
+
 def test_fused_equals_unfused():
     for (m, n, k) in [(300, 200, 1024), (64, 96, 48), (512, 512, 640)]:
         xb, wb = quantized_pair(m, n, k, seed=k)
