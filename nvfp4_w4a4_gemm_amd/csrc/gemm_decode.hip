@@ -273,22 +273,44 @@ __device__ __forceinline__ void dma4_lds(__amdgpu_buffer_rsrc_t rs, void* lds, u
 // the compiler wait for them, which would drain the ring at every tile.)
 constexpr int kMaxTiles = 8;
 
-template <int MT, int S>
+// With kARes (one M-tile, and M x K small enough) the token rows are not
+// staged with every weight stage: the whole quantised activation is loaded
+// into LDS once, with the same 256-byte segments and XOR slot order, and
+// the ring carries the weight alone (half the LDS a stage, so more
+// workgroups fit on a CU).
+constexpr int kAResMaxBytes = 16 * 1024;
+
+__host__ __device__ constexpr int decode_stage_bytes(int MT, bool ares) {
+  return (ares ? 1 : 1 + MT) * kTileBytes + 256;
+}
+// Resident activation: code segments rounded up to whole 1 KB DMAs, scale
+// segments to whole 256-byte DMAs (the last DMA's surplus lanes land in
+// the padding).
+__host__ __device__ constexpr int decode_ares_code_bytes(int M, int n_stages) {
+  return (M * n_stages + 3) / 4 * 4 * kStageCodes;
+}
+__host__ __device__ constexpr int decode_ares_bytes(int M, int n_stages) {
+  return decode_ares_code_bytes(M, n_stages) + (M * n_stages + 7) / 8 * 8 * kStageScales;
+}
+
+template <int MT, int S, bool kARes>
 __global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ alpha_a, const uint8_t* __restrict__ b_codes,
     const uint8_t* __restrict__ b_scales, const float* __restrict__ alpha_b,
     const float* __restrict__ alpha_b_rows, int M, int N, int K,
     float* __restrict__ y_f32, uint16_t* __restrict__ y_bf16, int64_t ld_y) {
-  constexpr int kTiles = 1 + MT;                       // B tile, then the A tiles
+  static_assert(!kARes || MT == 1, "resident activations take one M-tile");
+  constexpr int kTiles = kARes ? 1 : 1 + MT;           // B tile, then the A tiles
   // scale DMAs: 8 rows x 32 bytes of one tile each (all 64 lanes); wave w
   // takes halves w, w + 4, ...; a wave left without one reloads a valid
   // half into a slack area, so every wave counts the same loads
   constexpr int kScaleDmas = (2 * kTiles + kWaves - 1) / kWaves;
-  constexpr int kStage = kTiles * kTileBytes + 256;    // + slack
+  constexpr int kStage = decode_stage_bytes(MT, kARes);
   constexpr int kRed = kWaves * MT * 16 * 17 * 4;      // one tile's partial sums
   static_assert(kRed <= S * kStage, "the reduction fits in the ring");
-  __shared__ __align__(16) uint8_t lds[S * kStage];
+  // ring, then (kARes) the resident activation
+  extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
@@ -338,9 +360,12 @@ __global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
     const int rb = nb0 + dma_row < N ? nb0 + dma_row : N - 1;
     dma16_lds(rbc, base + wave * 1024,
               (uint32_t)(rb * row_codes) + 16u * dma_chunk + st * kStageCodes);
+    if (!kARes) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-      dma16_lds(rac, base + (1 + t) * kTileBytes + wave * 1024, a_code_off[t] + st * kStageCodes);
+      for (int t = 0; t < MT; ++t)
+        dma16_lds(rac, base + (1 + t) * kTileBytes + wave * 1024,
+                  a_code_off[t] + st * kStageCodes);
+    }
 #pragma unroll
     for (int d = 0; d < kScaleDmas; ++d) {
       const int half = d * kWaves + wave;
@@ -356,6 +381,34 @@ __global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
   };
   constexpr int kDmaPerStage = kTiles + kScaleDmas;
 
+  // resident activation: codes [M][n_stages * 256] (slot order as in the
+  // ring), then scales [M][n_stages * 32]; 256-byte code segments and
+  // 32-byte scale segments in row-major order, so one wave DMA moves four
+  // code segments (1 KB) or eight scale segments (256 bytes)
+  uint8_t* ares = lds + S * kStage;
+  const int ares_code_pitch = n_stages * kStageCodes;
+  const int ares_scale_base = decode_ares_code_bytes(M, n_stages);
+  const int ares_scale_pitch = n_stages * kStageScales;
+  if (kARes) {
+    const int code_dmas = (M * n_stages + 3) / 4;      // 4 segments each
+    for (int i = wave; i < code_dmas; i += kWaves) {
+      const int seg = 4 * i + (lane >> 4);
+      const int m = seg / n_stages < M ? seg / n_stages : M - 1;
+      const int st = seg / n_stages < M ? seg % n_stages : n_stages - 1;
+      const int chunk = r16 ^ (m & 15);
+      dma16_lds(rac, ares + i * 1024,
+                (uint32_t)(m * row_codes) + (uint32_t)st * kStageCodes + 16u * chunk);
+    }
+    const int scale_dmas = (M * n_stages + 7) / 8;     // 8 segments each
+    for (int i = wave; i < scale_dmas; i += kWaves) {
+      const int seg = 8 * i + (lane >> 3);
+      const int m = seg / n_stages < M ? seg / n_stages : M - 1;
+      const int st = seg / n_stages < M ? seg % n_stages : n_stages - 1;
+      dma4_lds(ras, ares + ares_scale_base + i * 256,
+               (uint32_t)(m * row_scales) + (uint32_t)st * kStageScales + 4u * (lane & 7));
+    }
+  }
+
   float4_t acc[kMaxTiles][MT];
 #pragma unroll
   for (int tt = 0; tt < kMaxTiles; ++tt)
@@ -367,9 +420,18 @@ __global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
   const int q = 4 * wave + (lane >> 4);                 // this lane's chunk of a stage
   const int rd_code = r16 * kStageCodes + ((q ^ r16) << 4);
   const int rd_scale = 16 * kStageCodes + r16 * kStageScales + 2 * q;
+  // resident activation: this lane's token row (rows past M read row M - 1,
+  // whose scales are zeroed)
+  const int am = r16 < M ? r16 : M - 1;
+  const int ares_code = am * ares_code_pitch + (((q ^ am) & 15) << 4);
+  const int ares_scale = ares_scale_base + am * ares_scale_pitch + 2 * q;
 
 #pragma unroll
   for (int g = 0; g < S - 1; ++g) issue(g);
+  if (kARes) {
+    // the resident activation is older than the ring's first S - 1 stages
+    __builtin_amdgcn_s_waitcnt(vm_wait((S - 1) * kDmaPerStage));
+  }
 
   int g = 0;
 #pragma unroll
@@ -391,11 +453,17 @@ __global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
         const uint32_t bs = *reinterpret_cast<const uint16_t*>(base + rd_scale);
         u32x4 ac[MT];
         uint32_t as[MT];
+        if (kARes) {
+          ac[0] = *reinterpret_cast<const u32x4*>(ares + ares_code + st * kStageCodes);
+          as[0] = *reinterpret_cast<const uint16_t*>(ares + ares_scale + st * kStageScales) &
+                  (a_ok[0] ? mask : 0u);
+        } else {
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const uint8_t* tl = base + (1 + t) * kTileBytes;
-          ac[t] = *reinterpret_cast<const u32x4*>(tl + rd_code);
-          as[t] = *reinterpret_cast<const uint16_t*>(tl + rd_scale) & (a_ok[t] ? mask : 0u);
+          for (int t = 0; t < MT; ++t) {
+            const uint8_t* tl = base + (1 + t) * kTileBytes;
+            ac[t] = *reinterpret_cast<const u32x4*>(tl + rd_code);
+            as[t] = *reinterpret_cast<const uint16_t*>(tl + rd_scale) & (a_ok[t] ? mask : 0u);
+          }
         }
         const uint32_t bw[4] = {bc.x, bc.y, bc.z, bc.w};
 #pragma unroll
@@ -451,37 +519,57 @@ __global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
   }
 }
 
+// Launches the LDS-staged kernel with the ring (and resident activation)
+// in dynamic LDS, on as many workgroups as fit at once (at most one per
+// column tile, and enough that none takes more than kMaxTiles tiles).
+template <int MT, int S, bool kARes>
+hipError_t launch_lds(const DecodeArgs& p, int lds_bytes, hipStream_t stream) {
+  static int cache_bytes[64], cache_wgs[64];
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const int slot = dev & 63;
+  if (cache_bytes[slot] != lds_bytes) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(w4a4_decode_lds_kernel<MT, S, kARes>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess)
+      return hipErrorInvalidValue;
+    int occ = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, w4a4_decode_lds_kernel<MT, S, kARes>,
+                                                     kThreads, lds_bytes) != hipSuccess ||
+        occ < 1)
+      occ = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 256;
+    cache_wgs[slot] = occ * cus;
+    cache_bytes[slot] = lds_bytes;
+  }
+  const int tiles = (int)((p.N + kCols - 1) / kCols);
+  int wgs = tiles < cache_wgs[slot] ? tiles : cache_wgs[slot];
+  const int need = (tiles + kMaxTiles - 1) / kMaxTiles;
+  if (wgs < need) wgs = need;
+  hipLaunchKernelGGL((w4a4_decode_lds_kernel<MT, S, kARes>), dim3((unsigned)wgs), dim3(kThreads),
+                     lds_bytes, stream, p.a_codes, p.a_scales, p.alpha_a, p.b_codes, p.b_scales,
+                     p.alpha_b, p.alpha_b_rows, (int)p.M, (int)p.N, (int)p.K, p.y_f32, p.y_bf16,
+                     p.ld_y);
+  return hipGetLastError();
+}
+
 template <int MT>
 hipError_t launch_mt(const DecodeArgs& p, hipStream_t stream) {
   const dim3 grid((unsigned)((p.N + kCols - 1) / kCols));
-  constexpr int kS = MT == 1 ? 8 : MT == 2 ? 5 : 3;
+  // ring depths (stages) measured best at these LDS footprints: the
+  // resident-activation kernel fits four workgroups a CU with 4 stages
+  constexpr int kS = MT == 1 ? 6 : MT == 2 ? 5 : 3;
+  constexpr int kSR = 4;
   if (p.K % 64 == 0 && std::getenv("NVFP4_DECODE_DIRECT") == nullptr) {
-    // persistent workgroups: as many as fit on the chip at once, at most
-    // one per column tile
-    static int per_cu_cache[64];
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    int& per_cu = per_cu_cache[dev & 63];
-    if (per_cu == 0) {
-      int occ = 0, cus = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, w4a4_decode_lds_kernel<MT, kS>,
-                                                       kThreads, 0) != hipSuccess || occ < 1)
-        occ = 1;
-      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-          cus < 1)
-        cus = 256;
-      per_cu = occ * cus;
+    const int n_stages = (int)((p.K / 2 + kStageCodes - 1) / kStageCodes);
+    if constexpr (MT == 1) {
+      const int64_t ares_bytes = (p.M * n_stages + 7) / 8 * 8 * (int64_t)(kStageCodes + kStageScales);
+      if (ares_bytes <= kAResMaxBytes)
+        return launch_lds<MT, kSR, true>(
+            p, kSR * decode_stage_bytes(MT, true) + decode_ares_bytes((int)p.M, n_stages), stream);
     }
-    // as many workgroups as fit at once, at most one per column tile, and
-    // enough that none takes more than kMaxTiles tiles
-    const int tiles = (int)((p.N + kCols - 1) / kCols);
-    int wgs = tiles < per_cu ? tiles : per_cu;
-    const int need = (tiles + kMaxTiles - 1) / kMaxTiles;
-    if (wgs < need) wgs = need;
-    const dim3 pgrid((unsigned)wgs);
-    hipLaunchKernelGGL((w4a4_decode_lds_kernel<MT, kS>), pgrid, dim3(kThreads), 0, stream,
-                       p.a_codes, p.a_scales, p.alpha_a, p.b_codes, p.b_scales, p.alpha_b,
-                       p.alpha_b_rows, (int)p.M, (int)p.N, (int)p.K, p.y_f32, p.y_bf16, p.ld_y);
+    return launch_lds<MT, kS, false>(p, kS * decode_stage_bytes(MT, false), stream);
   } else if (p.K % 32 == 0)
     hipLaunchKernelGGL((w4a4_decode_kernel<MT, true>), grid, dim3(kThreads), 0, stream,
                        p.a_codes, p.a_scales, p.alpha_a, p.b_codes, p.b_scales, p.alpha_b,
