@@ -23,6 +23,7 @@ bounded sample on the host cores.  One JSON line goes to stdout.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -66,35 +67,50 @@ def parse():
 
 
 class Timer:
-    """HIP events around launches on torch's current stream (the library's)."""
+    """HIP events around launches on torch's current stream (the library's).
+
+    The events are created, and recorded once, before the timed region
+    (`prepare`), so that the timed loop only records existing events: event
+    creation inside the loop stalls the host now and then."""
 
     def __init__(self, torch):
         self.torch = torch
-        self.pairs = {}
+        self.pool = {}
+        self.used = {}
+
+    def prepare(self, name, count):
+        torch = self.torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(count)]
+        for s, e in evs:
+            s.record()
+            e.record()
+        self.pool[name] = evs
+        self.used[name] = 0
 
     def __call__(self, name):
-        torch = self.torch
         timer = self
 
         class _Ctx:
             def __enter__(self_):
-                self_.s = torch.cuda.Event(enable_timing=True)
-                self_.e = torch.cuda.Event(enable_timing=True)
+                i = timer.used[name]
+                self_.s, self_.e = timer.pool[name][i]
+                timer.used[name] = i + 1
                 self_.s.record()
 
             def __exit__(self_, *a):
                 self_.e.record()
-                timer.pairs.setdefault(name, []).append((self_.s, self_.e))
         return _Ctx()
 
     def total_ms(self, name):
-        return sum(s.elapsed_time(e) for s, e in self.pairs.get(name, []))
+        return sum(s.elapsed_time(e) for s, e in self.pool[name][:self.used[name]])
 
     def count(self, name):
-        return len(self.pairs.get(name, []))
+        return self.used[name]
 
     def reset(self):
-        self.pairs = {}
+        for name in self.used:
+            self.used[name] = 0
 
 
 def time_ms(torch, fn, reps, warmup):
@@ -166,16 +182,21 @@ def main():
         def __exit__(self, *a):
             return False
 
-    def w4a4_step(i, timed):
+    def w4a4_step(i, timed, every=False):
+        # timed: HIP events around the Q|K|V GEMM (the roofline kernel);
+        # every: around every launch (a separate pass: many live events make
+        # the runtime stall the host, so the timed region keeps them few)
         x = xs[i % args.rotate]
-        ctx = timer if timed else (lambda name: _Null())
-        with ctx("quantize"):
+        null = lambda name: _Null()
+        ctx_main = timer if timed else null
+        ctx_rest = timer if every else null
+        with ctx_rest("quantize"):
             nv.nvfp4_quantize_act(x["X_qkv"], out=qbuf["X_qkv"], workspace=workspace)
-        with ctx("gemm_qkv"):
+        with ctx_main("gemm_qkv"):
             nv.w4a4_gemm_multi(qbuf["X_qkv"], qkv, f32=False, y_bf16=outs["qkv"])
-        with ctx("quantize"):
+        with ctx_rest("quantize"):
             nv.nvfp4_quantize_act(x["X_o"], out=qbuf["X_o"], workspace=workspace)
-        with ctx("gemm_o"):
+        with ctx_rest("gemm_o"):
             nv.w4a4_gemm(qbuf["X_o"], wq["W_o"], f32=False, y_bf16=outs["o"])
 
     def bf16_step(i):
@@ -199,9 +220,15 @@ def main():
         return (time.perf_counter() - t) * 1e3 / steps
 
     # --- the timed region: K steps of the W4A4 layer -----------------------
+    # Python's full garbage collections walk every object torch created at
+    # import (tens of ms); frozen, those objects are skipped, so a long run
+    # does not stall the host mid-loop
+    gc.collect()
+    gc.freeze()
     log(f"timing W4A4 layer: {args.warmup} warmup + {args.steps} steps")
     for i in range(args.warmup):
         w4a4_step(i, timed=False)
+    timer.prepare("gemm_qkv", args.steps)
     torch.cuda.synchronize()
     timer.reset()
     t = time.perf_counter()
@@ -209,8 +236,16 @@ def main():
         w4a4_step(i, timed=True)
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t) * 1e3 / args.steps
-
     qkv_ms = timer.total_ms("gemm_qkv") / timer.count("gemm_qkv")
+
+    # the other launches' durations, from a second pass of the same steps
+    passes = min(args.steps, 20)
+    for name, per_step in (("quantize", 2), ("gemm_o", 1)):
+        timer.prepare(name, per_step * passes)
+    torch.cuda.synchronize()
+    for i in range(passes):
+        w4a4_step(i, timed=False, every=True)
+    torch.cuda.synchronize()
     o_ms = timer.total_ms("gemm_o") / timer.count("gemm_o")
     quant_ms = timer.total_ms("quantize") / timer.count("quantize")
     gemm_ms_step = qkv_ms + o_ms
@@ -242,6 +277,9 @@ def main():
     bf16_ms = time_steps(bf16_step, args.steps, args.warmup)
     blas_ms = time_steps(blas_step, args.steps, args.warmup)
     log(f"BF16 baseline step {bf16_ms:.3f} ms; hipBLASLt step {blas_ms:.3f} ms")
+
+    log("timing decode-shaped W4A4 GEMMs (w4a4_gemm_decode) against hipBLASLt BF16")
+    decode = decode_block(nv, torch, dev, workspace, args.steps, args.warmup)
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -293,6 +331,7 @@ def main():
                  "tflops": round(flops_step / (gemm_ms_step * 1e-3) / 1e12, 2),
                  "qkv_ms": round(qkv_ms, 4), "o_ms": round(o_ms, 4),
                  "o_tflops": round(o_tflops, 2)},
+        "decode": decode,
         "bf16_baseline": {"ms_per_step": round(bf16_ms, 4),
                           "speedup_layer": round(bf16_ms / ms_step, 3),
                           "speedup_gemm_only": round(bf16_ms / gemm_ms_step, 3),
@@ -303,6 +342,61 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x_host, w_host, args.cpu_rows, flops_step, m)
     print(json.dumps(result), flush=True)
+
+
+def decode_block(nv, torch, dev, workspace, steps, warmup):
+    """Decode-shaped W4A4 GEMMs of the same model (Qwen3-8B): the attention
+    projections (Q|K|V stacked 6144x4096, then O 4096x4096) and the MLP
+    (gate|up stacked 24576x4096, then down 4096x12288) at 1 and 16 tokens,
+    each pair of launches timed with HIP events.  The kernel streams the
+    NVFP4 weight (0.5625 bytes a weight), so the rate is weight bytes over
+    time against HBM.  Weights are seeded N(0, 0.02) draws made on the
+    device (the timing does not depend on their values), with enough copies
+    rotated (> 512 MB) that they come from HBM, not from the 256 MB MALL;
+    hipBLASLt (torch.matmul) on BF16 copies of the same weights is timed
+    beside it."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2024)
+    parts = {"attention": [(6144, 4096), (4096, 4096)], "mlp": [(24576, 4096), (4096, 12288)]}
+    rows = []
+    for part, shapes in parts.items():
+        wbytes = sum(n * k * 9 // 16 for n, k in shapes)
+        copies = max(2, (576 << 20) // wbytes)
+        bf_copies = max(2, (576 << 20) // sum(n * k * 2 for n, k in shapes))
+        bf = [[(torch.randn(n, k, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+               for n, k in shapes] for _ in range(bf_copies)]
+        q0 = [nv.nvfp4_quantize_weights(w, workspace=workspace) for w in bf[0]]
+        qs = [[nv.NVFP4Tensor(q.alpha.clone(), q.scales.clone(), q.codes.clone()) for q in q0]
+              for _ in range(copies)]
+        for tokens in (1, 16):
+            acts = [(torch.randn(tokens, k, device=dev, generator=gen)).to(torch.bfloat16)
+                    for _, k in shapes]
+            qa = [nv.nvfp4_quantize_act(a, workspace=workspace) for a in acts]
+            ys = [torch.empty(tokens, n, dtype=torch.bfloat16, device=dev) for n, _ in shapes]
+
+            def w4a4(i):
+                w = qs[i % copies]
+                for j in range(len(shapes)):
+                    nv.w4a4_gemm_decode(qa[j], w[j], f32=False, y_bf16=ys[j])
+
+            def blas(i):
+                w = bf[i % bf_copies]
+                for j in range(len(shapes)):
+                    torch.matmul(acts[j], w[j].t())
+
+            t = time_ms(torch, w4a4, max(steps, 20), warmup) * 1e3
+            tb = time_ms(torch, blas, max(steps, 20), warmup) * 1e3
+            gbps = wbytes / (t * 1e-6) / 1e9
+            rows.append({"part": part, "tokens": tokens,
+                         "shapes_nk": [list(x) for x in shapes],
+                         "us": round(t, 2), "weight_gbps": round(gbps, 1),
+                         "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                         "hipblaslt_bf16_us": round(tb, 2), "speedup_vs_hipblaslt": round(tb / t, 3)})
+            log(f"decode {part} x{tokens}: {t:.1f} us ({gbps:.0f} GB/s of NVFP4 weight); "
+                f"hipBLASLt BF16 {tb:.1f} us; x{tb / t:.2f}")
+        del bf, qs, q0
+        torch.cuda.empty_cache()
+    return {"kernel": "w4a4_gemm_decode", "bytes_per_weight": 0.5625, "rows": rows}
 
 
 def sweep(args):
