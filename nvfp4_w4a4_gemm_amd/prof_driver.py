@@ -5,7 +5,10 @@ Runs, on cuda:0, with nothing else in between:
      calibration of FETCH_SIZE / WRITE_SIZE against known bytes;
   2. the quantiser (amax, prepare, quantize) on X_qkv 8192 x 4096, three times;
   3. the stacked Q|K|V W4A4 GEMM 8192 x 6144 x 4096 (BF16 out), three times;
-  4. the BF16 comparison GEMM of the same shape, three times.
+  4. the BF16 comparison GEMM of the same shape, three times;
+  5. the decode-shaped W4A4 GEMM (w4a4_gemm_decode) of one token against the
+     stacked gate|up weight 24576 x 4096 (seeded N(0, 0.02) made on the
+     device), three times.
 Usage: rocprofv3 --pmc FETCH_SIZE -d OUT -o NAME -- python3 nvfp4_w4a4_gemm_amd/prof_driver.py
 """
 import os
@@ -46,6 +49,20 @@ def main():
     print("bf16 gemm 8192x6144x4096 x3", flush=True)
     for _ in range(3):
         nv.bf16_gemm_baseline(x, w, f32=False)
+    torch.cuda.synchronize()
+    print("w4a4 decode gemm 1x24576x4096 x3", flush=True)
+    del w
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    wgu = (torch.randn(24576, 4096, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+    qgu = nv.nvfp4_quantize_weights(wgu, workspace=ws)
+    del wgu
+    xt = (torch.randn(1, 4096, device=dev, generator=gen)).to(torch.bfloat16)
+    qt = nv.nvfp4_quantize_act(xt, workspace=ws)
+    yd = torch.empty(1, 24576, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        nv.w4a4_gemm_decode(qt, qgu, f32=False, y_bf16=yd)
     torch.cuda.synchronize()
     print("done", flush=True)
 
