@@ -43,11 +43,23 @@ notes of the repository):
   R8  two codes per byte, element 2j in the low nibble; rows are stored
       K-contiguous; scales are bytes, row-major [rows][K/16].
 
+* The normalisation whose output feeds a quantised projection, for the
+  quantiser fused into its producer.  The pages' models (Qwen3-8B,
+  Qwen3.5-9B, Gemma-4; paper.rainbus.top digest, 实验结果) normalise the input
+  of each attention and MLP block with RMSNorm; the pages do not define it.
+
+  R16 y_i = x_i * gamma_i / sqrt(mean_j(x_j^2) + eps) over each row, in
+      exact real arithmetic rounded once to BF16 (RNE); here: the sum of
+      the (exact) squares correctly rounded (math.fsum), then float64, a
+      few roundings of 2**-53 before the single BF16 rounding.
+
 Parity pins: every function here is checked by ``tests/test_oracle.py``
 against hand-worked blocks (``tests/golden/``), an exact rational
 brute force, closed forms and invariants.  No function is "parity unpinned".
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -305,6 +317,25 @@ def bf16_gemm_reference(x_bits: np.ndarray, w_bits: np.ndarray):
     w = bf16_to_f64(w_bits)
     y, bound = gemm_ref(x, w)
     return y, bound, f64_to_bf16_bits(y)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm producing the quantised activation (reading R16)
+# ---------------------------------------------------------------------------
+
+def rmsnorm(x_bits: np.ndarray, gamma_bits: np.ndarray, eps: float):
+    """Row-wise RMSNorm of BF16 x [rows][K] with BF16 weights gamma [K].
+
+    Returns (y, y_bits): the float64 values x*gamma/sqrt(mean(x^2)+eps) and
+    their BF16 rounding (RNE, one rounding).  Each row's sum of squares is
+    the correctly rounded sum of the exact squares (math.fsum)."""
+    x = bf16_to_f64(x_bits)
+    g = bf16_to_f64(gamma_bits)
+    k = x.shape[1]
+    ss = np.array([math.fsum(row * row) for row in x], dtype=np.float64)
+    inv = 1.0 / np.sqrt(ss / k + np.float64(eps))
+    y = x * inv[:, None] * g[None, :]
+    return y, f64_to_bf16_bits(y)
 
 
 def _why_float64_is_exact():
