@@ -278,6 +278,10 @@ def main():
     blas_ms = time_steps(blas_step, args.steps, args.warmup)
     log(f"BF16 baseline step {bf16_ms:.3f} ms; hipBLASLt step {blas_ms:.3f} ms")
 
+    log("timing RMSNorm with the quantiser fused in, against RMSNorm then quantise")
+    fused_norm = rmsnorm_block(nv, torch, [x["X_qkv"] for x in xs], workspace, args.steps,
+                               args.warmup)
+
     log("timing decode-shaped W4A4 GEMMs (w4a4_gemm_decode) against hipBLASLt BF16")
     decode = decode_block(nv, torch, dev, workspace, args.steps, args.warmup)
 
@@ -331,6 +335,7 @@ def main():
                  "tflops": round(flops_step / (gemm_ms_step * 1e-3) / 1e12, 2),
                  "qkv_ms": round(qkv_ms, 4), "o_ms": round(o_ms, 4),
                  "o_tflops": round(o_tflops, 2)},
+        "rmsnorm_quantize": fused_norm,
         "decode": decode,
         "bf16_baseline": {"ms_per_step": round(bf16_ms, 4),
                           "speedup_layer": round(bf16_ms / ms_step, 3),
@@ -342,6 +347,37 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x_host, w_host, args.cpu_rows, flops_step, m)
     print(json.dumps(result), flush=True)
+
+
+def rmsnorm_block(nv, torch, xs, workspace, steps, warmup):
+    """RMSNorm of the layer's activation (8192 x 4096, rotated copies) with
+    the quantiser fused in, against the unfused pair torch RMSNorm (BF16 out)
+    then nvfp4_quantize_act.  Algorithmic bytes: 2 + 2 + 0.5625 an element
+    fused (x read twice, codes and scales written), 2 + 2 + 2 + 2.5625
+    unfused."""
+    m, k = xs[0].shape
+    gen = torch.Generator(device=xs[0].device)
+    gen.manual_seed(99)
+    g = (1.0 + 0.1 * torch.randn(k, device=xs[0].device, generator=gen)).to(torch.bfloat16)
+    out = nv.nvfp4_rmsnorm_quantize_act(xs[0], g, 1e-6, workspace=workspace)
+    out2 = nv.nvfp4_quantize_act(xs[0], workspace=workspace)
+
+    def fused(i):
+        nv.nvfp4_rmsnorm_quantize_act(xs[i % len(xs)], g, 1e-6, out=out, workspace=workspace)
+
+    def unfused(i):
+        yn = torch.nn.functional.rms_norm(xs[i % len(xs)], (k,), g, 1e-6)
+        nv.nvfp4_quantize_act(yn, out=out2, workspace=workspace)
+
+    tf = time_ms(torch, fused, max(steps, 20), warmup) * 1e3
+    tu = time_ms(torch, unfused, max(steps, 20), warmup) * 1e3
+    gbps = m * k * 4.5625 / (tf * 1e-6) / 1e9
+    log(f"RMSNorm+quantise fused {tf:.1f} us ({gbps:.0f} GB/s); torch RMSNorm then quantise "
+        f"{tu:.1f} us; x{tu / tf:.2f}")
+    return {"kernel": "rmsnorm_amax_kernel + prepare_kernel + rmsnorm_quantize_kernel",
+            "shape": [m, k], "us": round(tf, 2), "gbps": round(gbps, 1),
+            "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes_per_elem": 4.5625,
+            "unfused_us": round(tu, 2), "speedup_vs_unfused": round(tu / tf, 3)}
 
 
 def decode_block(nv, torch, dev, workspace, steps, warmup):

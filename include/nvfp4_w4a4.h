@@ -150,6 +150,38 @@ nvfp4_status_t w4a4_gemm_multi(const uint8_t* a_codes, const uint8_t* a_scales,
                                uint16_t* y_bf16, int64_t ld_y, hipStream_t stream);
 
 /*
+ * nvfp4_rmsnorm_quantize_act - RMSNorm with the activation quantiser fused
+ * into it: the normalised activation is produced as NVFP4 (codes, scales,
+ * alpha) without a BF16 tensor in between.  The pages' models (Qwen3-8B,
+ * Qwen3.5-9B, Gemma-4; paper.rainbus digest, 实验结果) normalise each block's
+ * input with RMSNorm before the quantised projections; the pages do not
+ * define it, and the standard definition is taken:
+ *
+ *   y[m][k] = RNE_bf16( x[m][k] * r_m * gamma[k] ),
+ *   r_m     = 1 / sqrt( (1/K) sum_k x[m][k]^2 + eps )       (float32)
+ *
+ * and y is quantised exactly as nvfp4_quantize_act quantises a BF16 tensor
+ * (alpha from the amax of |y| unless alpha_in is given; 方法步骤详情 step (3)).
+ *
+ *   x_bf16      [M][ld_x] BF16 (16-byte aligned, ld_x * 2 a multiple of 16)
+ *   gamma_bf16  [K] BF16 weights (16-byte aligned)
+ *   K           a multiple of 16, at most 8192 (the row is held in registers)
+ *   eps         >= 0
+ *   alpha_in, alpha_out, codes, scales, workspace: as nvfp4_quantize_act
+ *   y_bf16      nullable: when set, y itself is also written, [M][ld_y]
+ *               (16-byte aligned, ld_y a multiple of 8, ld_y >= K)
+ * The two passes read x twice (the row's r is computed again, by the same
+ * arithmetic, so both passes see the same y).  Errors and ownership as for
+ * nvfp4_quantize_act.
+ */
+nvfp4_status_t nvfp4_rmsnorm_quantize_act(const void* x_bf16, const void* gamma_bf16, int64_t M,
+                                          int64_t K, int64_t ld_x, float eps,
+                                          const float* alpha_in, float* alpha_out,
+                                          uint8_t* codes, uint8_t* scales, uint16_t* y_bf16,
+                                          int64_t ld_y, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+
+/*
  * w4a4_gemm_decode - the W4A4 GEMM at decode shape: M <= 64 token rows
  * against a whole NVFP4 weight matrix, Y = A . B^T with the same arithmetic
  * and outputs as w4a4_gemm.  This is the decode step of the uniform-NVFP4

@@ -26,6 +26,9 @@ _SIGNATURES = {
                            _c_void, _c_void, _c_size, _c_void],
     "nvfp4_quantize_weights": [_c_void, _c_i64, _c_i64, _c_i64, _c_i64, _c_void, _c_void,
                                _c_void, _c_void, _c_size, _c_void],
+    "nvfp4_rmsnorm_quantize_act": [_c_void, _c_void, _c_i64, _c_i64, _c_i64, ctypes.c_float,
+                                   _c_void, _c_void, _c_void, _c_void, _c_void, _c_i64,
+                                   _c_void, _c_size, _c_void],
     "nvfp4_tensor_alpha": [_c_void, _c_i64, _c_i64, _c_i64, _c_void, _c_void, _c_size,
                            _c_void],
     "w4a4_gemm": [_c_void, _c_void, _c_void, _c_void, _c_void, _c_void, _c_i64, _c_i64,
@@ -139,6 +142,34 @@ def nvfp4_quantize_act(x: torch.Tensor, alpha_in: torch.Tensor | None = None,
     ws = workspace if workspace is not None else new_workspace(dev)
     _call("nvfp4_quantize_act", _ptr(x), m, k, x.stride(0), _ptr(alpha_in), _ptr(out.alpha),
           _ptr(out.codes), _ptr(out.scales), _ptr(ws), ws.numel(), _stream(dev))
+    return out
+
+
+def nvfp4_rmsnorm_quantize_act(x: torch.Tensor, gamma: torch.Tensor, eps: float,
+                               alpha_in: torch.Tensor | None = None,
+                               out: NVFP4Tensor | None = None, y_out: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None) -> NVFP4Tensor:
+    """RMSNorm of a BF16 activation [M, K] with weights gamma [K], produced
+    directly as NVFP4 (alpha from the normalised tensor unless given); y_out
+    (BF16 [M, K] view) also receives the normalised values when given."""
+    _check_bf16_2d(x, "x")
+    m, k = x.shape
+    if gamma.dtype != torch.bfloat16 or gamma.shape != (k,) or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous bfloat16 vector of length K")
+    if y_out is not None:
+        _check_bf16_2d(y_out, "y_out")
+        if tuple(y_out.shape) != (m, k):
+            raise ValueError("y_out must be [M, K]")
+    dev = x.device
+    if out is None:
+        out = NVFP4Tensor(torch.empty(1, dtype=torch.float32, device=dev),
+                          torch.empty(m, k // 16, dtype=torch.uint8, device=dev),
+                          torch.empty(m, k // 2, dtype=torch.uint8, device=dev))
+    ws = workspace if workspace is not None else new_workspace(dev)
+    _call("nvfp4_rmsnorm_quantize_act", _ptr(x), _ptr(gamma), m, k, x.stride(0),
+          ctypes.c_float(eps), _ptr(alpha_in), _ptr(out.alpha), _ptr(out.codes),
+          _ptr(out.scales), _ptr(y_out), y_out.stride(0) if y_out is not None else 0,
+          _ptr(ws), ws.numel(), _stream(dev))
     return out
 
 

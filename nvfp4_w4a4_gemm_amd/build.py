@@ -17,7 +17,8 @@ INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 OUT = os.path.join(PKG, "libnvfp4_w4a4.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "quantize.hip", "gemm_w4a4.hip", "gemm_decode.hip", "gemm_bf16.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "rmsnorm_quant.hip", "gemm_w4a4.hip", "gemm_decode.hip",
+           "gemm_bf16.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

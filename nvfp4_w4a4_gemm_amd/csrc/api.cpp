@@ -133,6 +133,55 @@ nvfp4_status_t nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K, int6
                          workspace_bytes, stream);
 }
 
+nvfp4_status_t nvfp4_rmsnorm_quantize_act(const void* x_bf16, const void* gamma_bf16, int64_t M,
+                                          int64_t K, int64_t ld_x, float eps,
+                                          const float* alpha_in, float* alpha_out,
+                                          uint8_t* codes, uint8_t* scales, uint16_t* y_bf16,
+                                          int64_t ld_y, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
+  if (alpha_out == nullptr) return NVFP4_ERR_NULL;
+  if (M > 0 && (x_bf16 == nullptr || gamma_bf16 == nullptr || codes == nullptr ||
+                scales == nullptr))
+    return NVFP4_ERR_NULL;
+  if (K > nvfp4::kRmsMaxK || !(eps >= 0.0f) || eps > 3.0e38f) return NVFP4_ERR_SHAPE;
+  nvfp4_status_t st = check_source(x_bf16, M, K, ld_x, 1);
+  if (st != NVFP4_OK) return st;
+  if (M > 0 && !aligned(gamma_bf16, 16)) return NVFP4_ERR_ALIGN;
+  if (y_bf16 != nullptr && M > 0) {
+    if (ld_y < K) return NVFP4_ERR_SHAPE;
+    if (!aligned(y_bf16, 16) || ld_y % 8 != 0) return NVFP4_ERR_ALIGN;
+  }
+  if (workspace == nullptr || workspace_bytes < kWorkspaceBytes) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
+  if (M > 0 && !aligned(codes, 8)) return NVFP4_ERR_ALIGN;
+  if ((st = check_device()) != NVFP4_OK) return st;
+
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  nvfp4::RmsQuantArgs a;
+  a.x = static_cast<const uint16_t*>(x_bf16);
+  a.gamma = static_cast<const uint16_t*>(gamma_bf16);
+  a.M = M;
+  a.K = K;
+  a.ld_x = ld_x;
+  a.eps = eps;
+  a.ws = w;
+  a.codes = codes;
+  a.scales = scales;
+  a.y_out = y_bf16;
+  a.ld_y = ld_y;
+  int n_partials = 0;
+  if (alpha_in == nullptr && M > 0) {
+    a.amax_pass = true;
+    if (nvfp4::launch_rmsnorm_quant(a, stream) != hipSuccess) return NVFP4_ERR_LAUNCH;
+    n_partials = nvfp4::rmsnorm_amax_grid(M);
+  }
+  if (nvfp4::launch_prepare(w + nvfp4::kWsPartials, n_partials, alpha_in, alpha_out, w, stream) !=
+      hipSuccess)
+    return NVFP4_ERR_LAUNCH;
+  a.amax_pass = false;
+  return launched(nvfp4::launch_rmsnorm_quant(a, stream));
+}
+
 nvfp4_status_t nvfp4_quantize_weights(const void* w_bf16, int64_t N, int64_t K,
                                       int64_t stride_n, int64_t stride_k, float* alpha_out,
                                       uint8_t* codes, uint8_t* scales, void* workspace,

@@ -49,6 +49,23 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k,
                            const uint8_t* ws, uint8_t* codes, uint8_t* scales,
                            hipStream_t stream);
 
+// ---- RMSNorm with the quantiser fused in ------------------------------------
+struct RmsQuantArgs {
+  const uint16_t* x;         // BF16 [M][ld_x]
+  const uint16_t* gamma;     // BF16 [K]
+  int64_t M, K, ld_x;
+  float eps;
+  uint8_t* ws;               // quantiser workspace (partials, tables)
+  uint8_t* codes;
+  uint8_t* scales;
+  uint16_t* y_out;           // nullable BF16 [M][ld_y]
+  int64_t ld_y;
+  bool amax_pass;            // true: the amax pass, false: the quantise pass
+};
+constexpr int64_t kRmsMaxK = 8192;
+int rmsnorm_amax_grid(int64_t M);
+hipError_t launch_rmsnorm_quant(const RmsQuantArgs& args, hipStream_t stream);
+
 // ---- GEMMs -----------------------------------------------------------------
 struct W4A4Args {
   const uint8_t* a_codes;

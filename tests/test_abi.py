@@ -34,7 +34,7 @@ def test_header_declares_the_four_entry_points():
     names = header_functions()
     for n in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "w4a4_gemm", "bf16_gemm_baseline",
               "w4a4_gemm_multi", "w4a4_gemm_grouped", "w4a4_gemm_fused_act",
-              "w4a4_gemm_decode"):
+              "w4a4_gemm_decode", "nvfp4_rmsnorm_quantize_act"):
         assert n in names
 
 
@@ -138,6 +138,36 @@ def test_gemm_multi_validation(lib):
     assert f(*bad) == SHAPE
     bad = list(args); bad[3] = p(4)
     assert f(*bad) == ALIGN
+
+
+@needs_lib
+def test_rmsnorm_quantize_validation(lib):
+    f = lib.nvfp4_rmsnorm_quantize_act
+    # x, gamma, M, K, ld_x, eps, alpha_in, alpha_out, codes, scales, y, ld_y, ws, ws_bytes, stream
+    args = [p(), p(), 64, 4096, 4096, 1e-6, None, p(), p(), p(), None, 0, p(), WS, None]
+    assert f(*args) == UNSUPPORTED
+    with_y = list(args); with_y[10] = p(); with_y[11] = 4096
+    assert f(*with_y) == UNSUPPORTED
+    bad = list(args); bad[1] = None                           # gamma required
+    assert f(*bad) == NULL
+    bad = list(args); bad[3] = 8192 + 16                      # row beyond the register budget
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[3] = 40
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[5] = -1.0                           # eps must be >= 0
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[5] = float("nan")
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[1] = p(8)                           # gamma 16-byte aligned
+    assert f(*bad) == ALIGN
+    bad = list(with_y); bad[11] = 4000                        # ld_y < K
+    assert f(*bad) == SHAPE
+    bad = list(with_y); bad[10] = p(2)
+    assert f(*bad) == ALIGN
+    bad = list(args); bad[13] = 100
+    assert f(*bad) == WORKSPACE
+    zero = list(args); zero[2] = 0                            # M = 0: alpha of nothing
+    assert f(*zero) == UNSUPPORTED
 
 
 @needs_lib

@@ -1,0 +1,82 @@
+"""RMSNorm with the quantiser fused in (nvfp4_rmsnorm_quantize_act) against
+the oracle.
+
+The kernel's normalised values y are compared with the oracle's RMSNorm
+(reading R16, exact up to float64 roundings, one BF16 rounding): equal or
+adjacent BF16 values (the kernel's float32 sum and reciprocal square root
+can put a value on the other side of a BF16 midpoint).  The quantisation of
+those y is then compared bit for bit: alpha, scale bytes and codes equal the
+oracle's quantisation of the kernel's own y.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import nvfp4_oracle as orc
+from nvfp4_w4a4_gemm_amd import binding as nv
+from nvfp4_w4a4_gemm_amd.workloads import workload
+
+from test_gpu_parity import bf16_ordered, dev_bf16, host_bits, normal_bits
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def gamma_bits(k, seed):
+    g = (1.0 + 0.1 * np.random.default_rng(seed).standard_normal(k)).astype(np.float32)
+    return orc.f64_to_bf16_bits(g)
+
+
+def check(xb, gb, eps, alpha_in=None, rows=None):
+    m, k = xb.shape
+    x = dev_bf16(xb)
+    g = torch.from_numpy(gb.view(np.int16)).to(DEV).view(torch.bfloat16)
+    y = torch.empty(m, k, dtype=torch.bfloat16, device=DEV)
+    a_in = None if alpha_in is None else torch.tensor([alpha_in], dtype=torch.float32, device=DEV)
+    q = nv.nvfp4_rmsnorm_quantize_act(x, g, eps, alpha_in=a_in, y_out=y)
+    q2 = nv.nvfp4_rmsnorm_quantize_act(x, g, eps, alpha_in=a_in)     # without y
+    torch.cuda.synchronize()
+    yk = host_bits(y)
+    sel = np.arange(m) if rows is None else rows
+    _, yref = orc.rmsnorm(xb[sel], gb, eps)
+    d = np.abs(bf16_ordered(yk[sel]) - bf16_ordered(yref))
+    assert d.max() <= 1, f"normalised values differ by {d.max()} BF16 ulp"
+    # quantisation of the kernel's own y: bit-exact (alpha from the whole y)
+    alpha = np.float32(alpha_in) if alpha_in is not None else orc.tensor_scale(orc.bf16_to_f64(yk))
+    assert q.alpha.item() == float(alpha)
+    ref = orc.quantize(yk[sel], alpha=alpha)
+    s = q.scales.cpu().numpy()[sel]
+    c = q.codes.cpu().numpy()[sel]
+    assert np.array_equal(s, ref[1]), np.argwhere(s != ref[1])[:4]
+    assert np.array_equal(c, ref[2]), np.argwhere(c != ref[2])[:4]
+    assert torch.equal(q.codes, q2.codes) and torch.equal(q.scales, q2.scales)
+    assert torch.equal(q.alpha, q2.alpha)
+    return int((d == 1).sum())
+
+
+@pytest.mark.parametrize("m,k", [(64, 4096), (37, 2816), (5, 16), (300, 5120), (1, 8192),
+                                 (200, 1040), (130, 48), (9, 6144)])
+def test_rmsnorm_quantize_matches_oracle(m, k):
+    xb = normal_bits(m, k, seed=m * 7 + k)
+    off = check(xb, gamma_bits(k, k), 1e-6)
+    print(f"[{m}x{k}] {off} of {m * k} normalised values one BF16 ulp from the oracle")
+
+
+def test_rmsnorm_quantize_zero_rows_tiny_eps_and_given_alpha():
+    m, k = 48, 1024
+    xb = normal_bits(m, k, seed=5)
+    xb[3] = 0                      # a zero row: y = 0 (eps > 0)
+    xb[7] = 0x8000                 # -0.0 everywhere: y = -0.0, code 0x8
+    check(xb, gamma_bits(k, 6), 1e-5)
+    check(xb, gamma_bits(k, 6), 0.25)                  # eps that matters
+    check(xb, gamma_bits(k, 6), 1e-5, alpha_in=2.0 ** -9)
+
+
+def test_rmsnorm_quantize_full_size_sampled_rows():
+    """The layer's X_qkv (8192 x 4096, outlier channels) with sampled rows
+    checked against the oracle, alpha and every code of those rows exact."""
+    xb = workload(2).tensors["X_qkv"].full()
+    rows = np.unique(np.concatenate([[0, xb.shape[0] - 1],
+                                     np.random.default_rng(9).choice(xb.shape[0], 96, False)]))
+    check(xb, gamma_bits(xb.shape[1], 10), 1e-6, rows=rows)
