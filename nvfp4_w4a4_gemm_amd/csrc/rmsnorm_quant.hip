@@ -212,6 +212,130 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quantize_kernel(
   });
 }
 
+// ---- streaming variant (rows longer than 5120) -----------------------------
+// The row is not held in registers: it is read once for the sum of squares
+// and chunk by chunk again for y (the second read finds it in L2), gamma is
+// read per chunk (L2), so a wave needs few registers.  The sum of
+// squares visits the chunks, and the words of a chunk, in the same order as
+// row_inv_rms, so r (and y) are the same bits as the register variant's.
+template <int CH>
+__device__ __forceinline__ float stream_inv_rms(const u32x4* __restrict__ xr, int nc, int lane,
+                                                int K, float eps) {
+  float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int c = lane + 64 * j;
+    const u32x4 v = c < nc ? xr[c] : u32x4{0u, 0u, 0u, 0u};
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xFFFF0000u);
+      part[i] = __builtin_fmaf(lo, lo, part[i]);
+      part[i] = __builtin_fmaf(hi, hi, part[i]);
+    }
+  }
+  float ss = (part[0] + part[1]) + (part[2] + part[3]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  return 1.0f / __builtin_sqrtf(ss / (float)K + eps);
+}
+
+template <int CH>
+__global__ __launch_bounds__(kThreads) void rmsnorm_amax_stream_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, int M, int K,
+    int64_t ld_x, float eps, uint32_t* __restrict__ partials) {
+  const int lane = threadIdx.x & 63;
+  const int nc = K / 8;
+  const u32x4* g4 = reinterpret_cast<const u32x4*>(gamma);
+  uint32_t m = 0;
+  for (int rowi = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6); rowi < M;
+       rowi += gridDim.x * kRowsPerBlock) {
+    const u32x4* xr = reinterpret_cast<const u32x4*>(x + rowi * ld_x);
+    const float r = stream_inv_rms<CH>(xr, nc, lane, K, eps);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nc) {
+        const u32x4 y = chunk_y(xr[c], g4[c], r);
+        m = pk_max_u16(m, pk_max_u16(pk_max_u16(y.x & 0x7FFF7FFFu, y.y & 0x7FFF7FFFu),
+                                     pk_max_u16(y.z & 0x7FFF7FFFu, y.w & 0x7FFF7FFFu)));
+      }
+    }
+  }
+  m = max(m & 0xFFFFu, m >> 16);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t red[kRowsPerBlock];
+  if (lane == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t v = red[0];
+#pragma unroll
+    for (int i = 1; i < kRowsPerBlock; ++i) v = max(v, red[i]);
+    partials[blockIdx.x] = v;
+  }
+}
+
+template <int CH>
+__global__ __launch_bounds__(kThreads) void rmsnorm_quantize_stream_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, int M, int K,
+    int64_t ld_x, float eps, const uint8_t* __restrict__ ws, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, uint16_t* __restrict__ y_out, int64_t ld_y) {
+  __shared__ __align__(16) uint8_t lds_sig[kSigLutN];
+  __shared__ __align__(16) uint8_t lds_code[kCodeLutN];
+  const int lane = threadIdx.x & 63;
+  const int nc = K / 8;
+  const u32x4* g4 = reinterpret_cast<const u32x4*>(gamma);
+  load_tables_to_lds(ws, lds_sig, lds_code, threadIdx.x, kThreads);
+  const BlockTables t = tables_from(ws, lds_sig, lds_code);
+  __syncthreads();
+  for (int rowi = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6); rowi < M;
+       rowi += gridDim.x * kRowsPerBlock) {
+    const u32x4* xr = reinterpret_cast<const u32x4*>(x + rowi * ld_x);
+    const float r = stream_inv_rms<CH>(xr, nc, lane, K, eps);
+    uint32_t* crow = reinterpret_cast<uint32_t*>(codes + (int64_t)rowi * (K / 2));
+    uint8_t* srow = scales + (int64_t)rowi * (K / 16);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = lane + 64 * j;
+      const bool ok = c < nc;
+      const u32x4 y = ok ? chunk_y(xr[c], g4[c], r) : u32x4{0u, 0u, 0u, 0u};
+      const uint32_t w[4] = {y.x, y.y, y.z, y.w};
+      uint32_t mag[8];
+      magnitudes<4>(w, t, mag);
+      uint32_t amax = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = max(amax, mag[i]);
+      amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0xB1, 0xF, 0xF, false));
+      CodeRow cr;
+      const uint32_t sb = block_scale(amax, t, cr);
+      const uint32_t o = codes8(mag, w, cr, t);
+      if (ok) {
+        crow[c] = o;
+        if ((lane & 1) == 0) srow[c >> 1] = (uint8_t)sb;
+        if (y_out != nullptr) reinterpret_cast<u32x4*>(y_out + rowi * ld_y)[c] = y;
+      }
+    }
+  }
+}
+
+template <int CH>
+hipError_t launch_stream(const RmsQuantArgs& a, hipStream_t stream) {
+  const int64_t blocks = (a.M + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (a.amax_pass) {
+    const int grid = (int)(blocks < kAmaxPartials ? blocks : kAmaxPartials);
+    hipLaunchKernelGGL((rmsnorm_amax_stream_kernel<CH>), dim3(grid), dim3(kThreads), 0, stream,
+                       a.x, a.gamma, (int)a.M, (int)a.K, a.ld_x, a.eps,
+                       reinterpret_cast<uint32_t*>(a.ws + kWsPartials));
+    return hipGetLastError();
+  }
+  const int grid = (int)(blocks < 2048 ? blocks : 2048);
+  hipLaunchKernelGGL((rmsnorm_quantize_stream_kernel<CH>), dim3(grid), dim3(kThreads), 0, stream,
+                     a.x, a.gamma, (int)a.M, (int)a.K, a.ld_x, a.eps, a.ws, a.codes, a.scales,
+                     a.y_out, a.ld_y);
+  return hipGetLastError();
+}
+
 template <int CH>
 hipError_t launch_ch(const RmsQuantArgs& a, hipStream_t stream) {
   // two rows held (the next one loading) where registers allow
@@ -264,8 +388,10 @@ hipError_t launch_rmsnorm_quant(const RmsQuantArgs& a, hipStream_t stream) {
   if (ch <= 6) return launch_ch<6>(a, stream);
   if (ch <= 8) return launch_ch<8>(a, stream);
   if (ch <= 10) return launch_ch<10>(a, stream);
-  if (ch <= 12) return launch_ch<12>(a, stream);
-  return launch_ch<16>(a, stream);
+  // longer rows: two would not fit in registers; streaming the row (measured
+  // 6% faster at K = 8192, slower below)
+  if (ch <= 12) return launch_stream<12>(a, stream);
+  return launch_stream<16>(a, stream);
 }
 
 }  // namespace nvfp4
