@@ -53,6 +53,15 @@ notes of the repository):
       the (exact) squares correctly rounded (math.fsum), then float64, a
       few roundings of 2**-53 before the single BF16 rounding.
 
+* The gated MLP activation H = SiLU(G) * U of the gate and up projections'
+  outputs, which the down projection's quantiser takes as its input (the
+  pages' models' MLPs; the configuration of the layer names the down input
+  "SiLU(gate) * up").
+
+  R17 H = RNE_bf16( g * u / (1 + exp(-g)) ) element by element, from the
+      projections' float32 outputs g and u, in float64 before the single
+      BF16 rounding.
+
 Parity pins: every function here is checked by ``tests/test_oracle.py``
 against hand-worked blocks (``tests/golden/``), an exact rational
 brute force, closed forms and invariants.  No function is "parity unpinned".
@@ -336,6 +345,16 @@ def rmsnorm(x_bits: np.ndarray, gamma_bits: np.ndarray, eps: float):
     inv = 1.0 / np.sqrt(ss / k + np.float64(eps))
     y = x * inv[:, None] * g[None, :]
     return y, f64_to_bf16_bits(y)
+
+
+def silu_mul(g: np.ndarray, u: np.ndarray):
+    """H = SiLU(g) * u (reading R17) from float32 (or float64) g and u:
+    returns (h, h_bits), the float64 values and their BF16 rounding."""
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        h = g * u / (1.0 + np.exp(-g))
+    return h, f64_to_bf16_bits(h)
 
 
 def _why_float64_is_exact():
