@@ -282,6 +282,9 @@ def main():
     fused_norm = rmsnorm_block(nv, torch, [x["X_qkv"] for x in xs], workspace, args.steps,
                                args.warmup)
 
+    log("timing the gate|up GEMM with SiLU(gate)*up and its quantiser fused in")
+    fused_silu = silu_block(nv, torch, qbuf["X_qkv"], dev, workspace, args.steps, args.warmup)
+
     log("timing decode-shaped W4A4 GEMMs (w4a4_gemm_decode) against hipBLASLt BF16")
     decode = decode_block(nv, torch, dev, workspace, args.steps, args.warmup)
 
@@ -336,6 +339,7 @@ def main():
                  "qkv_ms": round(qkv_ms, 4), "o_ms": round(o_ms, 4),
                  "o_tflops": round(o_tflops, 2)},
         "rmsnorm_quantize": fused_norm,
+        "gate_up_silu_quantize": fused_silu,
         "decode": decode,
         "bf16_baseline": {"ms_per_step": round(bf16_ms, 4),
                           "speedup_layer": round(bf16_ms / ms_step, 3),
@@ -378,6 +382,48 @@ def rmsnorm_block(nv, torch, xs, workspace, steps, warmup):
             "shape": [m, k], "us": round(tf, 2), "gbps": round(gbps, 1),
             "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes_per_elem": 4.5625,
             "unfused_us": round(tu, 2), "speedup_vs_unfused": round(tu / tf, 3)}
+
+
+def silu_block(nv, torch, qa, dev, workspace, steps, warmup):
+    """The MLP's gate|up projection of the same model at prefill (Qwen3-8B:
+    8192 tokens, 4096 -> 2 x 12288) with SiLU(gate) * up and H's quantiser
+    fused into the GEMM (w4a4_gemm_silu_mul_quantize), against the unfused
+    chain: the same GEMM writing BF16 gate|up, torch silu and multiply, then
+    nvfp4_quantize_act of H.  Weights are seeded N(0, 0.02) draws made on
+    the device."""
+    m, k = qa.rows, qa.k
+    hidden = 12288
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    qg, qu = [nv.nvfp4_quantize_weights(
+        (torch.randn(hidden, k, device=dev, generator=gen) * 0.02).to(torch.bfloat16),
+        workspace=workspace) for _ in range(2)]
+    stack = nv.interleave_gate_up(qg, qu)
+    n = 2 * hidden
+    ws = nv.silu_mul_workspace(m, n, dev)
+    qh, h = nv.w4a4_gemm_silu_mul_quantize(qa, stack, workspace=ws)
+    y = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    qh2 = nv.NVFP4Tensor(torch.empty_like(qh.alpha), torch.empty_like(qh.scales),
+                         torch.empty_like(qh.codes))
+
+    def fused(i):
+        nv.w4a4_gemm_silu_mul_quantize(qa, stack, h=h, out=qh, workspace=ws)
+
+    def unfused(i):
+        nv.w4a4_gemm_multi(qa, stack, f32=False, y_bf16=y)
+        v = y.view(m, n // 64, 2, 32)
+        hu = (torch.nn.functional.silu(v[:, :, 0]) * v[:, :, 1]).reshape(m, hidden)
+        nv.nvfp4_quantize_act(hu, out=qh2, workspace=workspace)
+
+    tf = time_ms(torch, fused, max(steps, 10), warmup)
+    tu = time_ms(torch, unfused, max(steps, 10), warmup)
+    flops = 2.0 * m * n * k
+    log(f"gate|up GEMM + SiLU*up + quantise fused {tf * 1e3:.1f} us "
+        f"({flops / (tf * 1e-3) / 1e12:.0f} TFLOP/s); unfused {tu * 1e3:.1f} us; x{tu / tf:.2f}")
+    return {"kernel": "w4a4_gemm_kernel<silu> + prepare_kernel + quantize_kernel",
+            "shape": [m, n, k], "ms": round(tf, 4),
+            "tflops": round(flops / (tf * 1e-3) / 1e12, 2),
+            "unfused_ms": round(tu, 4), "speedup_vs_unfused": round(tu / tf, 3)}
 
 
 def decode_block(nv, torch, dev, workspace, steps, warmup):

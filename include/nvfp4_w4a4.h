@@ -182,6 +182,39 @@ nvfp4_status_t nvfp4_rmsnorm_quantize_act(const void* x_bf16, const void* gamma_
                                           hipStream_t stream);
 
 /*
+ * w4a4_gemm_silu_mul_quantize - the gate|up projection of a gated MLP with
+ * the activation and the next quantiser fused in: the W4A4 GEMM's epilogue
+ * computes H = SiLU(gate) * up, the down projection's input, in BF16
+ * together with the amax of |H| per tile, then H is quantised to NVFP4 with
+ * alpha from those maxima (方法步骤详情 step (3)).  The pages' models
+ * (Qwen3-8B and its kin; paper.rainbus digest, 实验结果) use this gated MLP
+ * without defining it; the standard definition is taken.  The gate and up
+ * outputs never reach memory.
+ *
+ *   b_codes/b_scales  the gate and up weights interleaved in 32-row blocks:
+ *                     rows 64j .. 64j + 31 are gate rows 32j .. 32j + 31 and
+ *                     rows 64j + 32 .. 64j + 63 the up rows of the same
+ *                     units; N = 2 x hidden, a multiple of 64
+ *   alpha_b_rows      device float32 [N]: the tensor scale of each B row
+ *   h_bf16            [M][ld_h] BF16 (ld_h >= N/2, a multiple of 8, 16-byte
+ *                     aligned): H, written, then read by the quantiser
+ *   H[m][u] = RNE_bf16( g * v / (1 + exp(-g)) ), with g and v the float32
+ *             gate and up outputs (alpha_a alpha_b sum ...) of unit u
+ *   alpha_h_out, h_codes [M][N/4], h_scales [M][N/32]: H in NVFP4
+ *   workspace  at least w4a4_gemm_silu_mul_workspace_bytes(M, N) bytes
+ *             (16-byte aligned): the quantiser's tables and the tile maxima
+ * Other arguments, ownership and errors as for w4a4_gemm_multi.
+ */
+size_t w4a4_gemm_silu_mul_workspace_bytes(int64_t M, int64_t N);
+nvfp4_status_t w4a4_gemm_silu_mul_quantize(const uint8_t* a_codes, const uint8_t* a_scales,
+                                           const float* alpha_a, const uint8_t* b_codes,
+                                           const uint8_t* b_scales, const float* alpha_b_rows,
+                                           int64_t M, int64_t N, int64_t K, uint16_t* h_bf16,
+                                           int64_t ld_h, float* alpha_h_out, uint8_t* h_codes,
+                                           uint8_t* h_scales, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream);
+
+/*
  * w4a4_gemm_decode - the W4A4 GEMM at decode shape: M <= 64 token rows
  * against a whole NVFP4 weight matrix, Y = A . B^T with the same arithmetic
  * and outputs as w4a4_gemm.  This is the decode step of the uniform-NVFP4

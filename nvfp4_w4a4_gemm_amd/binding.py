@@ -35,6 +35,9 @@ _SIGNATURES = {
                   _c_i64, _c_void, _c_void, _c_i64, _c_void],
     "w4a4_gemm_multi": [_c_void, _c_void, _c_void, _c_void, _c_void, _c_void, _c_i64, _c_i64,
                         _c_i64, _c_void, _c_void, _c_i64, _c_void],
+    "w4a4_gemm_silu_mul_quantize": [_c_void, _c_void, _c_void, _c_void, _c_void, _c_void,
+                                    _c_i64, _c_i64, _c_i64, _c_void, _c_i64, _c_void, _c_void,
+                                    _c_void, _c_void, _c_size, _c_void],
     "w4a4_gemm_decode": [_c_void, _c_void, _c_void, _c_void, _c_void, _c_void, _c_void,
                          _c_i64, _c_i64, _c_i64, _c_void, _c_void, _c_i64, _c_void],
     "w4a4_gemm_grouped": [_c_void, _c_void, _c_void, _c_i64, _c_void, _c_void, _c_void,
@@ -47,7 +50,8 @@ _SIGNATURES = {
                            _c_void, _c_void, _c_i64, _c_void],
 }
 
-EXPORTS = sorted(list(_SIGNATURES) + ["nvfp4_status_string", "nvfp4_workspace_bytes"])
+EXPORTS = sorted(list(_SIGNATURES) + ["nvfp4_status_string", "nvfp4_workspace_bytes",
+                                      "w4a4_gemm_silu_mul_workspace_bytes"])
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_ALIGN",
           4: "NVFP4_ERR_UNSUPPORTED", 5: "NVFP4_ERR_LAUNCH", 6: "NVFP4_ERR_WORKSPACE"}
@@ -79,6 +83,8 @@ def lib() -> ctypes.CDLL:
         handle.nvfp4_status_string.restype = ctypes.c_char_p
         handle.nvfp4_workspace_bytes.argtypes = []
         handle.nvfp4_workspace_bytes.restype = ctypes.c_size_t
+        handle.w4a4_gemm_silu_mul_workspace_bytes.argtypes = [_c_i64, _c_i64]
+        handle.w4a4_gemm_silu_mul_workspace_bytes.restype = ctypes.c_size_t
         _lib = handle
     return _lib
 
@@ -270,6 +276,57 @@ def w4a4_gemm_multi(a: NVFP4Tensor, b: NVFP4Stack, f32: bool = True, bf16: bool 
           _ptr(b.scales), _ptr(b.alpha_rows), m, n, k, _ptr(y_f32), _ptr(y_bf16), ld,
           _stream(a.codes.device))
     return y_f32, y_bf16
+
+
+def interleave_gate_up(gate: NVFP4Tensor, up: NVFP4Tensor) -> NVFP4Stack:
+    """The gate and up weights (each [hidden, K], hidden a multiple of 32) as
+    one B operand for w4a4_gemm_silu_mul_quantize: 32-row blocks alternate,
+    gate rows 32j..32j+31 then up rows 32j..32j+31, with each row's tensor
+    scale in alpha_rows.  A row permutation of the quantised weights (offline
+    layout, no arithmetic)."""
+    hidden = gate.rows
+    if up.rows != hidden or up.k != gate.k or hidden % 32 != 0:
+        raise ValueError("gate and up must have the same shape, rows a multiple of 32")
+    nb = hidden // 32
+
+    def mix(a, b):
+        return torch.stack([a.view(nb, 32, -1), b.view(nb, 32, -1)], dim=1).reshape(2 * hidden, -1)
+
+    dev = gate.codes.device
+    ar = torch.stack([gate.alpha.expand(hidden).reshape(nb, 32),
+                      up.alpha.expand(hidden).reshape(nb, 32)], dim=1).reshape(2 * hidden)
+    return NVFP4Stack(mix(gate.codes, up.codes).contiguous(),
+                      mix(gate.scales, up.scales).contiguous(),
+                      ar.to(torch.float32).contiguous().to(dev), [0, 2 * hidden])
+
+
+def silu_mul_workspace(m: int, n: int, device) -> torch.Tensor:
+    return torch.empty(int(lib().w4a4_gemm_silu_mul_workspace_bytes(m, n)), dtype=torch.uint8,
+                       device=device)
+
+
+def w4a4_gemm_silu_mul_quantize(a: NVFP4Tensor, b: NVFP4Stack, h: torch.Tensor | None = None,
+                                out: NVFP4Tensor | None = None,
+                                workspace: torch.Tensor | None = None):
+    """H = SiLU(gate) * up of the interleaved gate|up weight b, produced by
+    the GEMM's epilogue, and H quantised to NVFP4 -> (NVFP4Tensor, H)."""
+    m, k = a.rows, a.k
+    n = b.rows
+    if b.k != k:
+        raise ValueError("operands disagree on K")
+    dev = a.codes.device
+    nh = n // 2
+    if h is None:
+        h = torch.empty(m, nh, dtype=torch.bfloat16, device=dev)
+    if out is None:
+        out = NVFP4Tensor(torch.empty(1, dtype=torch.float32, device=dev),
+                          torch.empty(m, nh // 16, dtype=torch.uint8, device=dev),
+                          torch.empty(m, nh // 2, dtype=torch.uint8, device=dev))
+    ws = workspace if workspace is not None else silu_mul_workspace(m, n, dev)
+    _call("w4a4_gemm_silu_mul_quantize", _ptr(a.codes), _ptr(a.scales), _ptr(a.alpha),
+          _ptr(b.codes), _ptr(b.scales), _ptr(b.alpha_rows), m, n, k, _ptr(h), h.stride(0),
+          _ptr(out.alpha), _ptr(out.codes), _ptr(out.scales), _ptr(ws), ws.numel(), _stream(dev))
+    return out, h
 
 
 DECODE_MAX_ROWS = 64

@@ -254,6 +254,9 @@ static nvfp4_status_t gemm_common(const uint8_t* a_codes, const uint8_t* a_scale
   a.a_bf16 = nullptr;
   a.ld_a = 0;
   a.ws = nullptr;
+  a.h_bf16 = nullptr;
+  a.ld_h = 0;
+  a.h_partials = nullptr;
   return launched(nvfp4::launch_w4a4(a, stream));
 }
 
@@ -273,6 +276,78 @@ nvfp4_status_t w4a4_gemm_multi(const uint8_t* a_codes, const uint8_t* a_scales,
   if (alpha_b_rows == nullptr) return NVFP4_ERR_NULL;
   return gemm_common(a_codes, a_scales, alpha_a, M, nullptr, b_codes, b_scales, nullptr,
                      alpha_b_rows, M, N, K, 1, nullptr, y_f32, y_bf16, ld_y, stream);
+}
+
+size_t w4a4_gemm_silu_mul_workspace_bytes(int64_t M, int64_t N) {
+  if (M < 0 || N < 0) return 0;
+  return kWorkspaceBytes + 4 * (size_t)nvfp4::w4a4_silu_tiles_max(M, N);
+}
+
+nvfp4_status_t w4a4_gemm_silu_mul_quantize(const uint8_t* a_codes, const uint8_t* a_scales,
+                                           const float* alpha_a, const uint8_t* b_codes,
+                                           const uint8_t* b_scales, const float* alpha_b_rows,
+                                           int64_t M, int64_t N, int64_t K, uint16_t* h_bf16,
+                                           int64_t ld_h, float* alpha_h_out, uint8_t* h_codes,
+                                           uint8_t* h_scales, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 16 != 0 || N % 64 != 0 || M >= kMaxDim || N >= kMaxDim ||
+      K >= kMaxDim)
+    return NVFP4_ERR_SHAPE;
+  if (alpha_h_out == nullptr) return NVFP4_ERR_NULL;
+  const int64_t nh = N / 2;
+  if (M > 0 && N > 0) {
+    if (!a_codes || !a_scales || !alpha_a || !b_codes || !b_scales || !alpha_b_rows || !h_bf16 ||
+        !h_codes || !h_scales)
+      return NVFP4_ERR_NULL;
+    if (ld_h < nh) return NVFP4_ERR_SHAPE;
+    if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(h_bf16, 16) || ld_h % 8 != 0)
+      return NVFP4_ERR_ALIGN;
+    if (K % 128 == 0 && (!aligned(a_scales, 8) || !aligned(b_scales, 8))) return NVFP4_ERR_ALIGN;
+    if (!aligned(h_codes, 8)) return NVFP4_ERR_ALIGN;
+    constexpr int64_t kMaxBytes = (int64_t(1) << 32) - 1;
+    if (M * (K / 2) > kMaxBytes || N * (K / 2) > kMaxBytes) return NVFP4_ERR_SHAPE;
+  }
+  if (workspace == nullptr || workspace_bytes < w4a4_gemm_silu_mul_workspace_bytes(M, N))
+    return NVFP4_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
+  nvfp4_status_t st = check_device();
+  if (st != NVFP4_OK) return st;
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  uint32_t* partials = reinterpret_cast<uint32_t*>(w + kWorkspaceBytes);
+  int n_partials = 0;
+  if (M > 0 && N > 0) {
+    nvfp4::W4A4Args a;
+    a.a_codes = a_codes;
+    a.a_scales = a_scales;
+    a.alpha_a = alpha_a;
+    a.a_row_index = nullptr;
+    a.b_codes = b_codes;
+    a.b_scales = b_scales;
+    a.alpha_b = nullptr;
+    a.alpha_b_rows = alpha_b_rows;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.num_groups = 1;
+    a.group_offsets = nullptr;
+    a.y_f32 = nullptr;
+    a.y_bf16 = nullptr;
+    a.ld_y = 0;
+    a.a_bf16 = nullptr;
+    a.ld_a = 0;
+    a.ws = nullptr;
+    a.h_bf16 = h_bf16;
+    a.ld_h = ld_h;
+    a.h_partials = partials;
+    if (nvfp4::launch_w4a4_silu(a, stream) != hipSuccess) return NVFP4_ERR_LAUNCH;
+    n_partials = (int)nvfp4::w4a4_tiles(M, N);
+  }
+  // alpha of H from the tiles' maxima, then H's codes and scales
+  if (nvfp4::launch_prepare(reinterpret_cast<const uint8_t*>(partials), n_partials, nullptr,
+                            alpha_h_out, w, stream) != hipSuccess)
+    return NVFP4_ERR_LAUNCH;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  return launched(nvfp4::launch_quantize(h_bf16, M, nh, ld_h, 1, w, h_codes, h_scales, stream));
 }
 
 nvfp4_status_t w4a4_gemm_decode(const uint8_t* a_codes, const uint8_t* a_scales,
@@ -368,6 +443,9 @@ nvfp4_status_t w4a4_gemm_fused_act(const void* x_bf16, int64_t ld_x, const float
   a.a_bf16 = static_cast<const uint16_t*>(x_bf16);
   a.ld_a = ld_x;
   a.ws = w;
+  a.h_bf16 = nullptr;
+  a.ld_h = 0;
+  a.h_partials = nullptr;
   return launched(nvfp4::launch_w4a4_fused(a, stream));
 }
 

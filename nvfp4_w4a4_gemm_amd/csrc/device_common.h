@@ -15,6 +15,7 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 // Quotient and remainder by a fixed divisor with one multiply-high
 // (round-up method; exact for every n < 2^31 and d < 2^31).

@@ -143,8 +143,26 @@ __device__ __forceinline__ bool tile_coord(int tile_m, const int64_t* offsets,
 // into LDS with the exact tables (quant_block.h) instead of loading codes.
 // kRing: LDS stages in the ring (3 or 4; loads run kRing - 1 stages ahead and
 // the next stage's fragments are read while this one computes).  kOcc: waves
-// per SIMD the register budget is sized for.
-template <int BM, int BN, bool kKAligned, bool kFused, int kRing, int kOcc>
+// per SIMD the register budget is sized for.  kSilu: B is a gate|up weight
+// interleaved in 32-row blocks (gate rows, then the up rows of the same 32
+// units) and the epilogue writes H = SiLU(gate) * up in BF16 ([M][N/2])
+// and the tile's amax of |H| instead of the projections' outputs.
+// SiLU(g) * u = g u / (1 + e^-g), with no overflow and no loss in the
+// float32 subnormal range.  With e = exp(-|g|) <= 1 and E = e 2^64 (normal
+// for |g| < 131, formed by the hardware exp2 as 2^(64 - |g| log2 e)):
+// g >= 0: H = g u / (1 + e); g < 0: H = (g u / (1 + e)) E 2^-64, the power
+// of two applied last so that the product keeps float32's relative
+// precision until the final rounding even where H is a float32 subnormal.
+// exp2 and the reciprocal are 1-ulp hardware approximations; with the
+// rounding of |g| log2 e the relative error of H stays below about 2^-17.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  constexpr float kLog2e = 1.44269504f;
+  const float big_e = __builtin_amdgcn_exp2f(__builtin_fmaf(fabsf(g), -kLog2e, 64.0f));
+  const float q = (g * u) * __builtin_amdgcn_rcpf(1.0f + big_e * 0x1p-64f);
+  return g >= 0.0f ? q : (q * big_e) * 0x1p-64f;
+}
+
+template <int BM, int BN, bool kKAligned, bool kFused, int kRing, int kOcc, bool kSilu = false>
 __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   constexpr int WM = BM / 2, WN = BN / 2;      // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;    // 32x32 fragments per wave
@@ -595,6 +613,100 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
       }
     }
   };
+  if constexpr (kSilu) {
+    // ---- gated activation: H = SiLU(g) * u --------------------------------
+    // Fragments 2jp and 2jp + 1 hold the gate and up outputs of the same 32
+    // units (B rows 64b .. 64b + 31 and 64b + 32 .. 64b + 63), so a lane
+    // finds g and u of an H value in its own registers.  H leaves through
+    // LDS bands as the outputs do; the amax of |H| over the tile's real
+    // rows and columns goes to h_partials[tile].
+    static_assert(TN % 2 == 0, "gate/up fragment pairs");
+    constexpr int HW = WN / 2;                       // H columns of the wave
+    constexpr int kPitchH = HW * 2 + 16;
+    static_assert(4 * kBandRows * kPitchH <= kRing * kStageBytes, "bands fit the ring");
+    uint8_t* bandh = lds + wave * (kBandRows * kPitchH);
+    uint8_t* wh = bandh + (4 * fh) * kPitchH + fr * 2;
+    const int64_t n_h = p.N / 2;
+    const int64_t hcol0 = (tc.n0 + wn) / 2;
+    constexpr int kPer = 8, kLanesPerRow = HW / kPer, kRowsPerQ = 64 / kLanesPerRow;
+    static_assert(64 % kLanesPerRow == 0, "a row is a whole number of lanes");
+    constexpr int kQ = kBandRows / kRowsPerQ;
+    const int lane_row = lane / kLanesPerRow, lane_col = (lane % kLanesPerRow) * kPer;
+    const bool interior_h = tc.m0 + BM <= tc.m_end && (tc.n0 + BN) / 2 <= n_h;
+    // |H| maxima of the lane, as two BF16 magnitudes (rows r and r + 1)
+    u16x2 hm2 = {0, 0};
+    // interior tiles skip the row and column masks of the maxima and the
+    // bounds-checked stores (a uniform choice, one copy of the code each)
+    auto silu_epilogue = [&](auto k_in) __attribute__((always_inline)) {
+      constexpr bool kIn = decltype(k_in)::value;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t row0 = tc.m0 + wm + 32 * i + kBandRows * h;
+          const int64_t lim = row_lim - row0 - 4 * fh;   // rows of the band this lane may count
+#pragma unroll
+          for (int jp = 0; jp < TN / 2; ++jp) {
+            const bool col_ok = hcol0 + 32 * jp + fr < n_h;
+#pragma unroll
+            for (int r = 8 * h; r < 8 * h + 8; r += 2) {
+              const int row = 8 * ((r >> 2) - 2 * h) + (r & 3);
+              const float g0 = acc[i][2 * jp][r] * scale[2 * jp];
+              const float g1 = acc[i][2 * jp][r + 1] * scale[2 * jp];
+              const float u0 = acc[i][2 * jp + 1][r] * scale[2 * jp + 1];
+              const float u1 = acc[i][2 * jp + 1][r + 1] * scale[2 * jp + 1];
+              const bf16x2_t b = __builtin_convertvector(
+                  (float2_t){silu_mul(g0, u0), silu_mul(g1, u1)}, bf16x2_t);
+              *reinterpret_cast<__bf16*>(wh + row * kPitchH + 32 * jp * 2) = b[0];
+              *reinterpret_cast<__bf16*>(wh + (row + 1) * kPitchH + 32 * jp * 2) = b[1];
+              uint32_t bits = __builtin_bit_cast(uint32_t, b) & 0x7FFF7FFFu;
+              if constexpr (!kIn)
+                bits &= (col_ok && row < lim ? 0xFFFFu : 0u) |
+                        (col_ok && row + 1 < lim ? 0xFFFF0000u : 0u);
+              hm2 = __builtin_elementwise_max(hm2, __builtin_bit_cast(u16x2, bits));
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
+          const uint8_t* src = bandh + lane_row * kPitchH + lane_col * 2;
+          uint16_t* dst = p.h_bf16 + (row0 + lane_row) * p.ld_h + hcol0 + lane_col;
+          const int64_t step = (int64_t)kRowsPerQ * p.ld_h;
+          if (kIn && p.vec_h) {
+#pragma unroll
+            for (int q = 0; q < kQ; ++q)
+              *reinterpret_cast<u32x4*>(dst + q * step) =
+                  *reinterpret_cast<const u32x4*>(src + q * kRowsPerQ * kPitchH);
+          } else {
+            const int64_t rows_left = row_lim - row0;
+            const int64_t cols_left = n_h - hcol0;
+#pragma unroll 1
+            for (int q = 0; q < kQ; ++q) {
+              const uint16_t* t = reinterpret_cast<const uint16_t*>(src + q * kRowsPerQ * kPitchH);
+              if (q * kRowsPerQ + lane_row < rows_left) {
+#pragma unroll 1
+                for (int k = 0; k < kPer; ++k)
+                  if (lane_col + k < cols_left) dst[q * step + k] = t[k];
+              }
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
+        }
+    };
+    if (interior_h)
+      silu_epilogue(std::true_type{});
+    else
+      silu_epilogue(std::false_type{});
+    uint32_t hmax = max((uint32_t)hm2[0], (uint32_t)hm2[1]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) hmax = max(hmax, (uint32_t)__shfl_xor((int)hmax, off));
+    __shared__ uint32_t hred[4];
+    if (lane == 0) hred[wave] = hmax;
+    __syncthreads();
+    if (tid == 0)
+      p.h_partials[blockIdx.y * gridDim.x + blockIdx.x] =
+          max(max(hred[0], hred[1]), max(hred[2], hred[3]));
+    return;
+  }
+
   auto epilogue = [&](auto k32, auto k16) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -615,41 +727,43 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   else epilogue(no{}, yes{});
 }
 
-template <int BM, int BN, bool kFused, int kRing, int kOcc>
+template <int BM, int BN, bool kFused, int kRing, int kOcc, bool kSilu = false>
 hipError_t launch_tiles(const W4A4Args& a, hipStream_t stream) {
   int tiles_m = (int)((a.M + BM - 1) / BM);
   if (a.group_offsets != nullptr) tiles_m += a.num_groups;
   const int tiles_n = (int)((a.N + BN - 1) / BN);
   dim3 grid(tiles_m, tiles_n);
   if (a.K % kBK == 0)
-    hipLaunchKernelGGL((w4a4_gemm_kernel<BM, BN, true, kFused, kRing, kOcc>), grid,
+    hipLaunchKernelGGL((w4a4_gemm_kernel<BM, BN, true, kFused, kRing, kOcc, kSilu>), grid,
                        dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((w4a4_gemm_kernel<BM, BN, false, kFused, kRing, kOcc>), grid,
+    hipLaunchKernelGGL((w4a4_gemm_kernel<BM, BN, false, kFused, kRing, kOcc, kSilu>), grid,
                        dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 // Tile choice: NVFP4_GEMM_TILE (256x256, 128x256, 128x128) overrides the
-// size-based default, for tuning.
-template <bool kFused>
+// size-based default, for tuning.  0: 256x256, 1: 128x256, 2: 128x128.
+int tile_choice(int64_t M, int64_t N) {
+  const char* env = std::getenv("NVFP4_GEMM_TILE");
+  if (env != nullptr && std::strcmp(env, "256x256") == 0) return 0;
+  if (env != nullptr && std::strcmp(env, "128x256") == 0) return 1;
+  if (env != nullptr && std::strcmp(env, "128x128") == 0) return 2;
+  const int64_t t0 = ((M + 255) / 256) * ((N + 255) / 256);
+  return t0 >= 256 ? 0 : 2;
+}
+
+template <bool kFused, bool kSilu = false>
 hipError_t launch_any(const W4A4Args& args, hipStream_t stream) {
   if (args.M == 0 || args.N == 0) return hipSuccess;
   W4A4Args a = args;
   a.vec_f32 = (reinterpret_cast<uintptr_t>(a.y_f32) % 16 == 0) && (a.ld_y * 4) % 16 == 0;
   a.vec_bf16 = (reinterpret_cast<uintptr_t>(a.y_bf16) % 16 == 0) && (a.ld_y * 2) % 16 == 0;
-  const char* env = std::getenv("NVFP4_GEMM_TILE");
-  int choice;
-  if (env != nullptr && std::strcmp(env, "256x256") == 0) choice = 0;
-  else if (env != nullptr && std::strcmp(env, "128x256") == 0) choice = 1;
-  else if (env != nullptr && std::strcmp(env, "128x128") == 0) choice = 2;
-  else {
-    const int64_t t0 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-    choice = t0 >= 256 ? 0 : 2;
-  }
-  if (choice == 0) return launch_tiles<256, 256, kFused, kFused ? 3 : 4, 1>(a, stream);
-  if (choice == 1) return launch_tiles<128, 256, kFused, 3, 1>(a, stream);
-  return launch_tiles<128, 128, kFused, 3, 2>(a, stream);
+  a.vec_h = (reinterpret_cast<uintptr_t>(a.h_bf16) % 16 == 0) && (a.ld_h * 2) % 16 == 0;
+  const int choice = tile_choice(a.M, a.N);
+  if (choice == 0) return launch_tiles<256, 256, kFused, kFused ? 3 : 4, 1, kSilu>(a, stream);
+  if (choice == 1) return launch_tiles<128, 256, kFused, 3, 1, kSilu>(a, stream);
+  return launch_tiles<128, 128, kFused, 3, 2, kSilu>(a, stream);
 }
 
 }  // namespace
@@ -660,6 +774,21 @@ hipError_t launch_w4a4(const W4A4Args& a, hipStream_t stream) {
 
 hipError_t launch_w4a4_fused(const W4A4Args& a, hipStream_t stream) {
   return launch_any<true>(a, stream);
+}
+
+hipError_t launch_w4a4_silu(const W4A4Args& a, hipStream_t stream) {
+  return launch_any<false, true>(a, stream);
+}
+
+int64_t w4a4_silu_tiles_max(int64_t M, int64_t N) {
+  // the smallest tile gives the most workgroups
+  return ((M + 127) / 128) * ((N + 127) / 128);
+}
+
+int64_t w4a4_tiles(int64_t M, int64_t N) {
+  const int c = tile_choice(M, N);
+  const int64_t bm = c == 0 ? 256 : 128, bn = c == 2 ? 128 : 256;
+  return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
 }  // namespace nvfp4

@@ -86,11 +86,19 @@ struct W4A4Args {
   const uint16_t* a_bf16;
   int64_t ld_a;
   const uint8_t* ws;              // prepared decision tables for alpha_a
+  // gated activation (launch_w4a4_silu): H [M][N/2] BF16 and the amax of
+  // |H| bits per tile (tile blockIdx.y * gridDim.x + blockIdx.x)
+  uint16_t* h_bf16;
+  int64_t ld_h;
+  uint32_t* h_partials;
   // set by the launcher: the output rows may be written 16 bytes at a time
-  int32_t vec_f32, vec_bf16;
+  int32_t vec_f32, vec_bf16, vec_h;
 };
 hipError_t launch_w4a4(const W4A4Args& args, hipStream_t stream);
 hipError_t launch_w4a4_fused(const W4A4Args& args, hipStream_t stream);
+hipError_t launch_w4a4_silu(const W4A4Args& args, hipStream_t stream);
+int64_t w4a4_silu_tiles_max(int64_t M, int64_t N);   // bound on h_partials entries
+int64_t w4a4_tiles(int64_t M, int64_t N);            // workgroups of a dense launch
 
 // Decode-shaped W4A4 GEMM (M <= 64): codes/scales/alphas as in W4A4Args.
 struct DecodeArgs {

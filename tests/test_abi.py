@@ -34,7 +34,8 @@ def test_header_declares_the_four_entry_points():
     names = header_functions()
     for n in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "w4a4_gemm", "bf16_gemm_baseline",
               "w4a4_gemm_multi", "w4a4_gemm_grouped", "w4a4_gemm_fused_act",
-              "w4a4_gemm_decode", "nvfp4_rmsnorm_quantize_act"):
+              "w4a4_gemm_decode", "nvfp4_rmsnorm_quantize_act", "w4a4_gemm_silu_mul_quantize",
+              "w4a4_gemm_silu_mul_workspace_bytes"):
         assert n in names
 
 
@@ -197,6 +198,39 @@ def test_gemm_decode_validation(lib):
     assert f(*bad) == SHAPE
     zero = list(args); zero[7] = 0
     assert f(*zero) == OK
+
+
+@needs_lib
+def test_gemm_silu_mul_validation(lib):
+    f = lib.w4a4_gemm_silu_mul_quantize
+    ws_need = lib.w4a4_gemm_silu_mul_workspace_bytes(300, 640)
+    assert ws_need == lib.nvfp4_workspace_bytes() + 4 * 3 * 5    # 128 x 128 tiles at most
+    assert lib.w4a4_gemm_silu_mul_workspace_bytes(-1, 64) == 0
+    # a_codes, a_scales, alpha_a, b_codes, b_scales, alpha_b_rows, M, N, K, h, ld_h,
+    # alpha_h, h_codes, h_scales, ws, ws_bytes, stream
+    args = [p(), p(), p(), p(), p(), p(), 300, 640, 512, p(), 320, p(), p(), p(), p(),
+            ws_need, None]
+    assert f(*args) == UNSUPPORTED
+    bad = list(args); bad[7] = 608                            # N = 2 x hidden, 32-unit blocks
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[8] = 40
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[10] = 312                           # ld_h < N / 2
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[10] = 324                           # 16-byte rows of H
+    assert f(*bad) == ALIGN
+    bad = list(args); bad[9] = p(2)
+    assert f(*bad) == ALIGN
+    bad = list(args); bad[5] = None                           # per-row tensor scales required
+    assert f(*bad) == NULL
+    bad = list(args); bad[11] = None
+    assert f(*bad) == NULL
+    bad = list(args); bad[15] = ws_need - 4
+    assert f(*bad) == WORKSPACE
+    bad = list(args); bad[14] = p(8)
+    assert f(*bad) == ALIGN
+    zero = list(args); zero[6] = 0                            # M = 0: alpha of nothing
+    assert f(*zero) == UNSUPPORTED
 
 
 @needs_lib

@@ -1,0 +1,111 @@
+"""The gate|up W4A4 GEMM with SiLU(gate) * up and the next quantiser fused in
+(w4a4_gemm_silu_mul_quantize) against the oracle.
+
+The fused kernel shares the GEMM's main loop with w4a4_gemm_multi, so its
+float32 gate and up values are those w4a4_gemm_multi writes for the same
+interleaved weight; those are checked against the oracle GEMM as any W4A4
+output.  H is compared with the oracle's gated activation (reading R17,
+float64, one BF16 rounding) of those values: equal or adjacent BF16 values
+(the kernel's float32 exp and divide can put H on the other side of a BF16
+midpoint).  The quantisation of H is compared bit for bit: alpha (from the
+kernel's per-tile maxima), scale bytes and codes equal the oracle's
+quantisation of the kernel's own H.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import nvfp4_oracle as orc
+from nvfp4_w4a4_gemm_amd import binding as nv
+
+from test_gpu_parity import (assert_gemm_close, assert_quant_equal, bf16_ordered, dev_bf16,
+                             host_bits, normal_bits)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def gate_up_columns(hidden):
+    """Columns of the interleaved output that hold gate and up of each unit."""
+    u = np.arange(hidden)
+    gate = (u // 32) * 64 + u % 32
+    return gate, gate + 32
+
+
+def run_case(m, hidden, k, seed, gate_std=0.02, up_std=0.02, check_gemm=False):
+    xb = normal_bits(m, k, seed=seed)
+    gb = normal_bits(hidden, k, seed=seed + 1, std=gate_std, outliers=False)
+    ub = normal_bits(hidden, k, seed=seed + 2, std=up_std, outliers=False)
+    qa = nv.nvfp4_quantize_act(dev_bf16(xb))
+    qg = nv.nvfp4_quantize_weights(dev_bf16(gb))
+    qu = nv.nvfp4_quantize_weights(dev_bf16(ub))
+    stack = nv.interleave_gate_up(qg, qu)
+    qh, h = nv.w4a4_gemm_silu_mul_quantize(qa, stack)
+    y32, _ = nv.w4a4_gemm_multi(qa, stack, bf16=False)
+    torch.cuda.synchronize()
+    gcol, ucol = gate_up_columns(hidden)
+    y = y32.cpu().numpy()
+    g, u = y[:, gcol], y[:, ucol]
+    if check_gemm:
+        ra = orc.quantize(xb)
+        for w, part in ((gb, g), (ub, u)):
+            ref, bound, ref16 = orc.w4a4_reference(ra, orc.quantize(w))
+            assert_gemm_close(torch.from_numpy(part), None, ref, bound, ref16)
+    _, h_ref = orc.silu_mul(g, u)
+    hb = host_bits(h)
+    diff = np.abs(bf16_ordered(hb) - bf16_ordered(h_ref))
+    assert diff.max(initial=0) <= 1, f"H off by {diff.max()} BF16 ulps at " \
+        f"{np.unravel_index(diff.argmax(), diff.shape)}"
+    assert (diff == 0).mean() > 0.99
+    assert_quant_equal(qh, orc.quantize(hb))
+    return g, hb
+
+
+@pytest.mark.parametrize("m,hidden,k", [(256, 1024, 1024), (300, 320, 512), (37, 96, 48),
+                                        (1, 32, 16), (129, 160, 1408)])
+def test_silu_mul_quantize_matches_oracle(m, hidden, k):
+    run_case(m, hidden, k, seed=m + hidden + k, check_gemm=(m * hidden * k <= 300 * 320 * 512))
+
+
+def test_silu_mul_large_tile_path():
+    # 256 x 256 tiles (>= 256 workgroups): H is checked on every row
+    run_case(2048, 4096, 256, seed=5)
+
+
+def test_silu_mul_saturating_gate():
+    """Gate values far into both tails of SiLU (exp(-g) overflows float32
+    for g < -88.7) and up values of both signs."""
+    g, hb = run_case(200, 256, 512, seed=9, gate_std=2.0, up_std=0.5)
+    assert g.min() < -90 and g.max() > 90
+    h = orc.bf16_to_f64(hb)
+    assert np.all(h[g < -120] == 0)
+
+
+def test_silu_mul_h_row_pitch():
+    m, hidden, k = 70, 96, 256
+    xb = normal_bits(m, k, seed=13)
+    qa = nv.nvfp4_quantize_act(dev_bf16(xb))
+    qg = nv.nvfp4_quantize_weights(dev_bf16(normal_bits(hidden, k, seed=14, std=0.05)))
+    qu = nv.nvfp4_quantize_weights(dev_bf16(normal_bits(hidden, k, seed=15, std=0.05)))
+    stack = nv.interleave_gate_up(qg, qu)
+    q1, h1 = nv.w4a4_gemm_silu_mul_quantize(qa, stack)
+    wide = torch.full((m, hidden + 40), -7.0, dtype=torch.bfloat16, device=DEV)
+    q2, h2 = nv.w4a4_gemm_silu_mul_quantize(qa, stack, h=wide[:, :hidden])
+    torch.cuda.synchronize()
+    assert torch.equal(h1.view(torch.int16), h2.view(torch.int16))
+    assert torch.all(wide[:, hidden:] == -7.0)
+    assert torch.equal(q1.codes, q2.codes) and torch.equal(q1.scales, q2.scales)
+    assert q1.alpha.item() == q2.alpha.item()
+
+
+def test_silu_mul_empty_rows():
+    k, hidden = 256, 64
+    qg = nv.nvfp4_quantize_weights(dev_bf16(normal_bits(hidden, k, seed=3)))
+    stack = nv.interleave_gate_up(qg, qg)
+    qa = nv.NVFP4Tensor(torch.zeros(1, dtype=torch.float32, device=DEV),
+                        torch.empty(0, k // 16, dtype=torch.uint8, device=DEV),
+                        torch.empty(0, k // 2, dtype=torch.uint8, device=DEV))
+    qh, h = nv.w4a4_gemm_silu_mul_quantize(qa, stack)
+    torch.cuda.synchronize()
+    assert h.shape == (0, hidden) and qh.alpha.item() == 0.0
