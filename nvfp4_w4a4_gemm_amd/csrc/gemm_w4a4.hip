@@ -461,8 +461,17 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
 #pragma unroll
   for (int st = 0; st < kRing - 1; ++st)
     if (st < nk) fill_stage(st, st);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  if constexpr (kKAligned && !kFused) {
+    // wait for stage 0 only; stages 1 .. kRing - 2 stay in flight
+    const int issued = nk < kRing - 1 ? nk : kRing - 1;
+    if (kRing == 4 && issued >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kDmaPerStage));
+    else if (issued >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerStage));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
   read_half0(0);
   read_half1(0);
   take_scales();
@@ -579,7 +588,8 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   // q * kRowsPerQ + lane_row, columns lane_col .. lane_col + kPer - 1 of the
   // band.  Straight-line 16-byte stores when the tile is inside the output
   // and rows are 16-byte aligned (a uniform test), else element by element
-  // with bounds checks.
+  // with bounds checks.  The 16-byte stores are non-temporal: this kernel
+  // never reads the output, so it need not sit dirty in L2 at the end.
   auto band_store = [&](auto* y, const uint8_t* band, int vec, int i, int h)
       __attribute__((always_inline)) {
     using T = typename std::remove_pointer<decltype(y)>::type;
@@ -597,8 +607,8 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
     if (interior && vec) {
 #pragma unroll
       for (int q = 0; q < kQ; ++q)
-        *reinterpret_cast<u32x4*>(dst + q * step) =
-            *reinterpret_cast<const u32x4*>(src + q * kRowsPerQ * kPitch);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(src + q * kRowsPerQ * kPitch),
+                                    reinterpret_cast<u32x4*>(dst + q * step));
     } else {
       const int64_t rows_left = row_lim - row0;
       const int64_t cols_left = p.N - (tc.n0 + wn);
