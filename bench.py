@@ -53,8 +53,10 @@ def source_hash(path):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the chip takes on the order of 100 ms of sustained load to settle its
+    # clocks; 200 layer steps (about 0.12 s) reach that steady state
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--rotate", type=int, default=4, help="input copies cycled over steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192,

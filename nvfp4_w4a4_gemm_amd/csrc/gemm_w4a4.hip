@@ -162,7 +162,8 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g >= 0.0f ? q : (q * big_e) * 0x1p-64f;
 }
 
-template <int BM, int BN, bool kKAligned, bool kFused, int kRing, int kOcc, bool kSilu = false>
+template <int BM, int BN, bool kKAligned, bool kFused, int kRing, int kOcc, bool kSilu = false,
+          bool kPersist = false>
 __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   constexpr int WM = BM / 2, WN = BN / 2;      // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;    // 32x32 fragments per wave
@@ -173,9 +174,27 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   __shared__ __align__(16) uint8_t lds[kRing * kStageBytes];
   __shared__ __align__(16) uint8_t lds_tables[kTableBytes];
 
+  // kPersist: workgroup b walks the linear tiles b, b + gridDim.x, ... (row
+  // tile fastest, as the 2-D grid orders them); the last three stages of a
+  // tile load the next tile's first three, so its prologue is hidden.
+  // tc is the tile being computed, tl the tile whose stages are being loaded.
+  const int tiles_m = (int)((p.M + BM - 1) / BM);
+  const int n_tiles = tiles_m * (int)((p.N + BN - 1) / BN);
+  int tile = kPersist ? (int)blockIdx.x : (int)(blockIdx.y * gridDim.x + blockIdx.x);
+  auto dense_coord = [&](int t, TileCoord& c) __attribute__((always_inline)) {
+    c.group = 0;
+    c.m0 = (int64_t)(t % tiles_m) * BM;
+    c.m_end = p.M;
+    c.n0 = (int64_t)(t / tiles_m) * BN;
+  };
   TileCoord tc;
-  if (!tile_coord<BM>(blockIdx.x, p.group_offsets, p.num_groups, p.M, tc)) return;
-  tc.n0 = (int64_t)blockIdx.y * BN;
+  if constexpr (kPersist) {
+    dense_coord(tile, tc);
+  } else {
+    if (!tile_coord<BM>(blockIdx.x, p.group_offsets, p.num_groups, p.M, tc)) return;
+    tc.n0 = (int64_t)blockIdx.y * BN;
+  }
+  TileCoord tl = tc;
 
   const int tid = threadIdx.x;
   // the wave index is uniform: keep it (and the DMA LDS addresses) in SGPRs
@@ -188,13 +207,13 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   const uint8_t* b_scales = p.b_scales + (int64_t)tc.group * p.N * ks;
 
   auto a_src_row = [&](int r) __attribute__((always_inline)) {
-    int64_t g = tc.m0 + r;
-    g = g < tc.m_end ? g : tc.m_end - 1;       // past the tile: clamp (not stored)
+    int64_t g = tl.m0 + r;
+    g = g < tl.m_end ? g : tl.m_end - 1;       // past the tile: clamp (not stored)
     if (!kFused && p.a_row_index) g = p.a_row_index[g];
     return g;
   };
   auto b_src_row = [&](int r) __attribute__((always_inline)) {
-    int64_t g = tc.n0 + r;
+    int64_t g = tl.n0 + r;
     return g < p.N ? g : p.N - 1;
   };
 
@@ -212,6 +231,8 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   static_assert(BM % 128 == 0 && BN % 128 == 0, "tile sizes");
   static_assert(kRing == 3 || kRing == 4, "ring depth");
   uint32_t a_cv[kACodeIns], b_cv[kBCodeIns], a_sv[kAScaleIns], b_sv[kBScaleIns];
+  // DMA source offsets of the rows of tile tl
+  auto set_offsets = [&]() __attribute__((always_inline)) {
 #pragma unroll
   for (int i = 0; i < kACodeIns; ++i) {
     const int row = (i * 4 + wave) * 16 + (lane >> 2);
@@ -234,6 +255,8 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
     const int row = (i * 4 + wave) * 32 + (lane >> 1);
     b_sv[i] = (uint32_t)(b_src_row(row) * ks + (lane & 1) * 4);
   }
+  };
+  set_offsets();
   const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.a_codes, 0xFFFFFFFFu);
   const __amdgpu_buffer_rsrc_t rs_as = make_rsrc(p.a_scales, 0xFFFFFFFFu);
   const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(b_codes, (uint32_t)(p.N * kc));
@@ -356,14 +379,11 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   };
 
   float16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
   const int nk = (int)((K + kBK - 1) / kBK);
+  // ring slot of stage st of the tile being computed
+  int ring0 = 0;
+  auto slot = [&](int st) __attribute__((always_inline)) { return (ring0 + st) % kRing; };
+  bool has_next = false;      // kPersist: the last stages load the next tile
   const int fr = lane & 31, fh = lane >> 5;
 
   // Raw fragments of one stage in two halves (code words of steps 0-3 and
@@ -429,16 +449,17 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ad[i], bd[j], acc[i][j], 0, 0, 0);
   };
-  // one MFMA, then a quarter of the next step's decode, and so on; the
-  // group's share of the stage DMA goes after its first MFMAs, and LDS reads
-  // (ds_lo <= MFMA index < ds_hi) one per MFMA, so no burst of loads holds
-  // up the in-order issue of the next MFMA
+  // one MFMA, then five of the next step's decode instructions (about a
+  // sixteenth of them), and so on; the group's share of the stage DMA goes
+  // after its first MFMAs, and LDS reads (ds_lo <= MFMA index < ds_hi) one
+  // per MFMA, so no burst of loads holds up the in-order issue of the next
+  // MFMA
   auto interleave = [&](int n_dma = 0, int ds_lo = 0, int ds_hi = 0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TM * TN; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i < n_dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
       if (i >= ds_lo && i < ds_hi) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -447,8 +468,8 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   auto dma_group = [&](int kt, int g) __attribute__((always_inline)) {
     if (!kSpread) return 0;
     int ahead = kt + kRing - 1;
-    uint8_t* base = lds + (ahead % kRing) * kStageBytes;
-    ahead = ahead < nk ? ahead : nk - 1;
+    uint8_t* base = lds + slot(ahead) * kStageBytes;
+    ahead = ahead < nk ? ahead : (has_next ? ahead - nk : nk - 1);
     int n = 0;
 #pragma unroll
     for (int idx = g * kDmaPer; idx < (g + 1) * kDmaPer && idx < kDmaPerStage; ++idx, ++n)
@@ -460,7 +481,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   // prologue: kRing - 1 stages in LDS
 #pragma unroll
   for (int st = 0; st < kRing - 1; ++st)
-    if (st < nk) fill_stage(st, st);
+    if (st < nk) fill_stage(slot(st), st);
   if constexpr (kKAligned && !kFused) {
     // wait for stage 0 only; stages 1 .. kRing - 2 stay in flight
     const int issued = nk < kRing - 1 ? nk : kRing - 1;
@@ -472,16 +493,35 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  read_half0(0);
-  read_half1(0);
+  for (;;) {                                   // tiles (one unless kPersist)
+  read_half0(slot(0));
+  read_half1(slot(0));
   take_scales();
   decode_step(0, a_cur, b_cur);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   for (int kt = 0; kt < nk; ++kt) {
+    if constexpr (kPersist) {
+      // from here on the DMA loads the next tile's stages 0, 1, 2 (the slots
+      // after this tile's last stage), if there is a next tile
+      if (kt == nk - (kRing - 1)) {
+        has_next = tile + (int)gridDim.x < n_tiles;
+        if (has_next) {
+          dense_coord(tile + (int)gridDim.x, tl);
+          set_offsets();
+        }
+      }
+    }
     const int ahead = kt + kRing - 1;           // the stage loaded this iteration
-    if (!kSpread && ahead < nk) fill_stage(ahead % kRing, ahead);
-    // the next stage's slot (read even on the last iteration, then unused)
-    const int nbuf = (kt + 1) % kRing;
+    if (!kSpread && ahead < nk) fill_stage(slot(ahead), ahead);
+    // the next stage's slot: read even on the last iteration, where it holds
+    // the next tile's stage 0 (kPersist) or is unused
+    const int nbuf = slot(kt + 1);
     int nd = dma_group(kt, 0);
     decode_step(1, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave(nd);
     nd = dma_group(kt, 1);
@@ -535,8 +575,23 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   // contiguous bytes of one output row and stores them.  Each wave has a
   // region of its own in the (now idle) ring; a wave's LDS operations
   // complete in order, so a band needs no barrier between writes and reads.
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no DMA still writing the ring
-  __syncthreads();                         // every wave is done with the ring
+  if constexpr (kPersist) {
+    // every wave is done with this tile's last slot (the bands go there; the
+    // next tile's loads into the other slots stay in flight)
+    __builtin_amdgcn_s_barrier();
+  } else {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no DMA still writing the ring
+    __syncthreads();                             // every wave is done with the ring
+  }
+  // The epilogue's lane-dependent addresses derive from an opaque copy of
+  // the lane index, so that in the tile walk they are formed here, per tile,
+  // instead of being hoisted out of it (they would stay live, and spill,
+  // across the main loop).
+  int lane_e = lane;
+  if constexpr (kPersist) asm volatile("" : "+v"(lane_e));
+  const int fr_e = lane_e & 31, fh_e = lane_e >> 5;
+  // kPersist: one output type, its bands in this tile's last slot
+  uint8_t* const band_base = kPersist ? lds + slot(nk - 1) * kStageBytes : lds;
   // alpha_a alpha_b 2^8 per fragment column (one alpha_b per B row when B
   // concatenates several tensors, else the group's)
   float scale[TN];
@@ -544,7 +599,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   for (int j = 0; j < TN; ++j) {
     float ab;
     if (p.alpha_b_rows) {
-      const int64_t col = tc.n0 + wn + 32 * j + fr;
+      const int64_t col = tc.n0 + wn + 32 * j + fr_e;
       ab = p.alpha_b_rows[col < p.N ? col : p.N - 1];
     } else {
       ab = p.alpha_b[tc.group];
@@ -557,15 +612,16 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   constexpr int kPitch32 = WN * 4 + 32, kPitch16 = WN * 2 + 16;   // padded rows
   constexpr int kBandBytes = kBandRows * (kPitch32 + kPitch16);
   static_assert(4 * kBandBytes <= kRing * kStageBytes, "epilogue bands fit the ring");
-  uint8_t* band32 = lds + wave * kBandBytes;
-  uint8_t* band16 = band32 + kBandRows * kPitch32;
+  static_assert(!kPersist || 4 * kBandRows * kPitch32 <= kStageBytes, "bands fit one slot");
+  uint8_t* band32 = band_base + wave * (kPersist ? kBandRows * kPitch32 : kBandBytes);
+  uint8_t* band16 = kPersist ? band32 : band32 + kBandRows * kPitch32;
   const bool interior = tc.m0 + BM <= tc.m_end && tc.n0 + BN <= p.N;
 
   // Band (i, h): rows 16h .. 16h + 15 of fragment row i, i.e. accumulator
   // registers r = 8h .. 8h + 7 (row 8(r/4) + 4(lane/32) + r%4).  Each lane
   // writes at a fixed base plus compile-time offsets.
-  uint8_t* w32 = band32 + (4 * fh) * kPitch32 + fr * 4;
-  uint8_t* w16 = band16 + (4 * fh) * kPitch16 + fr * 2;
+  uint8_t* w32 = band32 + (4 * fh_e) * kPitch32 + fr_e * 4;
+  uint8_t* w16 = band16 + (4 * fh_e) * kPitch16 + fr_e * 2;
   auto band_write = [&](int i, int h, auto k32, auto k16) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
@@ -599,7 +655,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
     constexpr int kRowsPerQ = 64 / kLanesPerRow;
     static_assert(64 % kLanesPerRow == 0, "a row is a whole number of lanes");
     constexpr int kQ = kBandRows / kRowsPerQ;
-    const int lane_row = lane / kLanesPerRow, lane_col = (lane % kLanesPerRow) * kPer;
+    const int lane_row = lane_e / kLanesPerRow, lane_col = (lane_e % kLanesPerRow) * kPer;
     const int64_t row0 = tc.m0 + wm + 32 * i + kBandRows * h;
     const uint8_t* src = band + lane_row * kPitch + lane_col * kE;
     T* dst = y + (row0 + lane_row) * p.ld_y + tc.n0 + wn + lane_col;
@@ -634,14 +690,14 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
     constexpr int HW = WN / 2;                       // H columns of the wave
     constexpr int kPitchH = HW * 2 + 16;
     static_assert(4 * kBandRows * kPitchH <= kRing * kStageBytes, "bands fit the ring");
-    uint8_t* bandh = lds + wave * (kBandRows * kPitchH);
-    uint8_t* wh = bandh + (4 * fh) * kPitchH + fr * 2;
+    uint8_t* bandh = band_base + wave * (kBandRows * kPitchH);
+    uint8_t* wh = bandh + (4 * fh_e) * kPitchH + fr_e * 2;
     const int64_t n_h = p.N / 2;
     const int64_t hcol0 = (tc.n0 + wn) / 2;
     constexpr int kPer = 8, kLanesPerRow = HW / kPer, kRowsPerQ = 64 / kLanesPerRow;
     static_assert(64 % kLanesPerRow == 0, "a row is a whole number of lanes");
     constexpr int kQ = kBandRows / kRowsPerQ;
-    const int lane_row = lane / kLanesPerRow, lane_col = (lane % kLanesPerRow) * kPer;
+    const int lane_row = lane_e / kLanesPerRow, lane_col = (lane_e % kLanesPerRow) * kPer;
     const bool interior_h = tc.m0 + BM <= tc.m_end && (tc.n0 + BN) / 2 <= n_h;
     // |H| maxima of the lane, as two BF16 magnitudes (rows r and r + 1)
     u16x2 hm2 = {0, 0};
@@ -654,10 +710,10 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int64_t row0 = tc.m0 + wm + 32 * i + kBandRows * h;
-          const int64_t lim = row_lim - row0 - 4 * fh;   // rows of the band this lane may count
+          const int64_t lim = row_lim - row0 - 4 * fh_e;   // rows of the band this lane may count
 #pragma unroll
           for (int jp = 0; jp < TN / 2; ++jp) {
-            const bool col_ok = hcol0 + 32 * jp + fr < n_h;
+            const bool col_ok = hcol0 + 32 * jp + fr_e < n_h;
 #pragma unroll
             for (int r = 8 * h; r < 8 * h + 8; r += 2) {
               const int row = 8 * ((r >> 2) - 2 * h) + (r & 3);
@@ -709,14 +765,12 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) hmax = max(hmax, (uint32_t)__shfl_xor((int)hmax, off));
     __shared__ uint32_t hred[4];
-    if (lane == 0) hred[wave] = hmax;
+    if (lane_e == 0) hred[wave] = hmax;
     __syncthreads();
     if (tid == 0)
-      p.h_partials[blockIdx.y * gridDim.x + blockIdx.x] =
+      p.h_partials[tile] =
           max(max(hred[0], hred[1]), max(hred[2], hred[3]));
-    return;
-  }
-
+  } else {
   auto epilogue = [&](auto k32, auto k16) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -735,6 +789,32 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   if (want32 && want16) epilogue(yes{}, yes{});
   else if (want32) epilogue(yes{}, no{});
   else epilogue(no{}, yes{});
+  }
+
+  if (!has_next) break;
+  // the next tile: its stage 0 has landed (the last iteration waited for
+  // it), its stages 1 and 2 are in flight.  Every wave's band reads end
+  // before the first loads into the bands' slot.
+  tile += (int)gridDim.x;
+  tc = tl;
+  ring0 = (ring0 + nk) % kRing;
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(63));   // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  }                                            // tiles
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 template <int BM, int BN, bool kFused, int kRing, int kOcc, bool kSilu = false>
@@ -742,6 +822,22 @@ hipError_t launch_tiles(const W4A4Args& a, hipStream_t stream) {
   int tiles_m = (int)((a.M + BM - 1) / BM);
   if (a.group_offsets != nullptr) tiles_m += a.num_groups;
   const int tiles_n = (int)((a.N + BN - 1) / BN);
+  // persistent walk: the DMA path with a 4-deep ring, dense, one output type
+  // (its bands fit one ring slot), at least 4 stages and two tiles per CU;
+  // NVFP4_GEMM_PERSIST=0 turns it off
+  if constexpr (kRing == 4 && !kFused) {
+    const char* env = std::getenv("NVFP4_GEMM_PERSIST");
+    const bool allowed = env == nullptr || std::strcmp(env, "0") != 0;
+    const int64_t n_tiles = (int64_t)tiles_m * tiles_n;
+    const int cus = cu_count();
+    if (allowed && a.K % kBK == 0 && a.K / kBK >= 4 && a.group_offsets == nullptr &&
+        a.a_row_index == nullptr && (kSilu || ((a.y_f32 != nullptr) != (a.y_bf16 != nullptr))) &&
+        n_tiles >= 2 * (int64_t)cus) {
+      hipLaunchKernelGGL((w4a4_gemm_kernel<BM, BN, true, false, kRing, kOcc, kSilu, true>),
+                         dim3(cus), dim3(kThreads), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   dim3 grid(tiles_m, tiles_n);
   if (a.K % kBK == 0)
     hipLaunchKernelGGL((w4a4_gemm_kernel<BM, BN, true, kFused, kRing, kOcc, kSilu>), grid,

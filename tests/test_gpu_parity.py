@@ -393,3 +393,51 @@ def test_bf16_baseline_grouped():
             continue
         y, bound, y16_ref = orc.bf16_gemm_reference(xb[lo:hi], wbs[e])
         assert_gemm_close(y32[lo:hi], y16[lo:hi], y, bound, y16_ref)
+
+
+# ---------------------------------------------------------------------------
+# persistent tile walk (256 x 256 tiles, at least two per compute unit, one
+# output type): the same bits as one workgroup per tile
+# ---------------------------------------------------------------------------
+
+def _with_persist(monkeypatch, on, fn):
+    if on:
+        monkeypatch.delenv("NVFP4_GEMM_PERSIST", raising=False)
+    else:
+        monkeypatch.setenv("NVFP4_GEMM_PERSIST", "0")
+    out = fn()
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("m,n,k,out", [(8192, 4096, 512, "bf16"), (8000, 4100, 512, "f32"),
+                                       (4096, 8448, 640, "bf16")])
+def test_w4a4_gemm_persistent_equals_grid(monkeypatch, m, n, k, out):
+    xb, wb = quantized_pair(m, n, k, seed=m + n + k + 3)
+    qa = nv.nvfp4_quantize_act(dev_bf16(xb))
+    qw = nv.nvfp4_quantize_weights(dev_bf16(wb))
+    f32, bf16 = out == "f32", out == "bf16"
+    run = lambda: nv.w4a4_gemm(qa, qw, f32=f32, bf16=bf16)
+    y_p = _with_persist(monkeypatch, True, run)
+    y_g = _with_persist(monkeypatch, False, run)
+    got, ref = (y_p[0], y_g[0]) if f32 else (y_p[1].view(torch.int16), y_g[1].view(torch.int16))
+    assert torch.equal(got, ref)
+    rows = np.array([0, 1, 255, 256, m // 2 + 7, m - 1])
+    ra = orc.quantize(xb)
+    y, bound, y16_ref = orc.w4a4_reference((ra[0], ra[1][rows], ra[2][rows]), orc.quantize(wb))
+    if f32:
+        assert_gemm_close(y_p[0][rows], None, y, bound, y16_ref)
+    else:
+        assert_gemm_close(None, y_p[1][rows], y, bound, y16_ref)
+
+
+def test_w4a4_gemm_multi_persistent_equals_grid(monkeypatch):
+    m, k = 8192, 512
+    parts = [normal_bits(n, k, seed=90 + i, std=std, outliers=False)
+             for i, (n, std) in enumerate(((4096, 0.02), (1024, 0.5), (1024, 3.0)))]
+    qa = nv.nvfp4_quantize_act(dev_bf16(normal_bits(m, k, seed=89)))
+    stack = nv.stack_tensors([nv.nvfp4_quantize_weights(dev_bf16(w)) for w in parts])
+    run = lambda: nv.w4a4_gemm_multi(qa, stack, f32=False)[1]
+    y_p = _with_persist(monkeypatch, True, run)
+    y_g = _with_persist(monkeypatch, False, run)
+    assert torch.equal(y_p.view(torch.int16), y_g.view(torch.int16))

@@ -109,3 +109,35 @@ def test_silu_mul_empty_rows():
     qh, h = nv.w4a4_gemm_silu_mul_quantize(qa, stack)
     torch.cuda.synchronize()
     assert h.shape == (0, hidden) and qh.alpha.item() == 0.0
+
+
+def test_silu_mul_persistent_equals_grid(monkeypatch):
+    """4096 tokens, hidden 4096: 512 tiles of 256 x 256, so the persistent
+    tile walk runs; H, alpha, codes and scales equal the one-workgroup-per-
+    tile launch bit for bit."""
+    m, hidden, k = 4096, 4096, 512
+    qa = nv.nvfp4_quantize_act(dev_bf16(normal_bits(m, k, seed=41)))
+    qg = nv.nvfp4_quantize_weights(dev_bf16(normal_bits(hidden, k, seed=42, std=0.05)))
+    qu = nv.nvfp4_quantize_weights(dev_bf16(normal_bits(hidden, k, seed=43, std=0.05)))
+    stack = nv.interleave_gate_up(qg, qu)
+    res = []
+    for on in (True, False):
+        if on:
+            monkeypatch.delenv("NVFP4_GEMM_PERSIST", raising=False)
+        else:
+            monkeypatch.setenv("NVFP4_GEMM_PERSIST", "0")
+        q, h = nv.w4a4_gemm_silu_mul_quantize(qa, stack)
+        torch.cuda.synchronize()
+        res.append((q, h))
+    (q1, h1), (q2, h2) = res
+    assert torch.equal(h1.view(torch.int16), h2.view(torch.int16))
+    assert q1.alpha.item() == q2.alpha.item()
+    assert torch.equal(q1.codes, q2.codes) and torch.equal(q1.scales, q2.scales)
+    rows = np.array([0, 255, 256, 2049, m - 1])
+    y32, _ = nv.w4a4_gemm_multi(qa, stack, bf16=False)
+    torch.cuda.synchronize()
+    gcol, ucol = gate_up_columns(hidden)
+    y = y32.cpu().numpy()[rows]
+    _, h_ref = orc.silu_mul(y[:, gcol], y[:, ucol])
+    d = np.abs(bf16_ordered(host_bits(h1)[rows]) - bf16_ordered(h_ref))
+    assert d.max() <= 1
