@@ -110,6 +110,9 @@ class Timer:
     def count(self, name):
         return self.used[name]
 
+    def times_ms(self, name):
+        return [s.elapsed_time(e) for s, e in self.pool[name][:self.used[name]]]
+
     def reset(self):
         for name in self.used:
             self.used[name] = 0
@@ -239,6 +242,10 @@ def main():
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t) * 1e3 / args.steps
     qkv_ms = timer.total_ms("gemm_qkv") / timer.count("gemm_qkv")
+    qkv_sorted = sorted(timer.times_ms("gemm_qkv"))
+    qkv_stats = {"mean": round(qkv_ms * 1e3, 1), "median": round(qkv_sorted[len(qkv_sorted) // 2] * 1e3, 1),
+                 "min": round(qkv_sorted[0] * 1e3, 1), "max": round(qkv_sorted[-1] * 1e3, 1),
+                 "launches": len(qkv_sorted)}
 
     # the other launches' durations, from a second pass of the same steps
     passes = min(args.steps, 20)
@@ -326,6 +333,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(qkv_tflops / MFMA_F16_PEAK_TFLOPS, 4),
             "traffic": traffic,
+            "launch_us": qkv_stats,
         },
         "quantize": {
             "gbps": round(quant_gbps, 1),
