@@ -141,3 +141,45 @@ def test_silu_mul_persistent_equals_grid(monkeypatch):
     _, h_ref = orc.silu_mul(y[:, gcol], y[:, ucol])
     d = np.abs(bf16_ordered(host_bits(h1)[rows]) - bf16_ordered(h_ref))
     assert d.max() <= 1
+
+
+def test_silu_mul_full_size_mlp_config():
+    """The gate|up projection of the Qwen3-8B-shaped MLP configuration at
+    full size (X 32768x4096 with outlier channels, gate and up 12288x4096 ~
+    N(0, 0.02)), in the launch configuration the benchmark times: alpha of H
+    exact against the oracle's amax of the kernel's whole H, then sampled
+    rows of H within one BF16 ulp of the oracle's SiLU*up of the kernel's
+    float32 gate/up, and their codes and scales bit-exact."""
+    from nvfp4_w4a4_gemm_amd.workloads import workload
+    from test_gpu_configs import oracle_alpha, sample
+    wl = workload(3)
+    x = nv.to_device_bf16(wl.tensors["X"].full(), DEV)
+    qa = nv.nvfp4_quantize_act(x)
+    qg = nv.nvfp4_quantize_weights(nv.to_device_bf16(wl.tensors["W_gate"].full(), DEV))
+    qu = nv.nvfp4_quantize_weights(nv.to_device_bf16(wl.tensors["W_up"].full(), DEV))
+    del x
+    stack = nv.interleave_gate_up(qg, qu)
+    del qg, qu
+    qh, h = nv.w4a4_gemm_silu_mul_quantize(qa, stack)
+    torch.cuda.synchronize()
+    m, hidden = h.shape
+    hb_all = host_bits(h)
+    alpha = oracle_alpha(hb_all)
+    assert qh.alpha.item() == float(alpha)
+    rows = sample(m, 64, 777, must=(int(np.argmax((hb_all & np.uint16(0x7FFF)).max(axis=1))),))
+    y32, _ = nv.w4a4_gemm_multi(qa, stack, bf16=False)
+    torch.cuda.synchronize()
+    y = y32.index_select(0, torch.from_numpy(rows).to(DEV)).cpu().numpy()
+    del y32
+    torch.cuda.empty_cache()
+    gcol, ucol = gate_up_columns(hidden)
+    _, h_ref = orc.silu_mul(y[:, gcol], y[:, ucol])
+    hb = hb_all[rows]
+    d = np.abs(bf16_ordered(hb) - bf16_ordered(h_ref))
+    assert d.max() <= 1
+    ref = orc.quantize(hb, alpha=alpha)
+    rows_t = torch.from_numpy(rows).to(DEV)
+    assert np.array_equal(qh.scales.index_select(0, rows_t).cpu().numpy(), ref[1])
+    assert np.array_equal(qh.codes.index_select(0, rows_t).cpu().numpy(), ref[2])
+    print(f"[mlp gate|up] {m}x{2 * hidden}x{qa.k}: alpha of H exact, {len(rows)} rows of H "
+          f"within one ulp ({int((d > 0).sum())} off by one), their codes and scales bit-exact")
