@@ -436,11 +436,45 @@ def silu_block(nv, torch, qa, dev, workspace, steps, warmup):
             "unfused_ms": round(tu, 4), "speedup_vs_unfused": round(tu / tf, 3)}
 
 
+def graph_ms(torch, fn, n, reps, check=None):
+    """fn(0) .. fn(n - 1) captured once in a HIP graph and replayed reps
+    times: ms per fn call with no host launch cost between the kernels.
+    check(), if given, returns a tensor the calls write; every replay must
+    reproduce the eager result bit for bit."""
+    for i in range(n):
+        fn(i)
+    torch.cuda.synchronize()
+    ref = check().clone() if check is not None else None
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        if check is not None and not torch.equal(check(), ref):
+            raise RuntimeError("graph replay differs from the eager launches")
+        fn(0)                                   # eager work between replays
+        torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / (reps * n)
+
+
 def decode_block(nv, torch, dev, workspace, steps, warmup):
     """Decode-shaped W4A4 GEMMs of the same model (Qwen3-8B): the attention
     projections (Q|K|V stacked 6144x4096, then O 4096x4096) and the MLP
     (gate|up stacked 24576x4096, then down 4096x12288) at 1 and 16 tokens,
-    each pair of launches timed with HIP events.  The kernel streams the
+    each pair of launches timed with HIP events around replays of a HIP
+    graph of the launches over all weight copies (a decode step's kernels
+    are a few microseconds each, less than the host's cost to launch them
+    one by one from Python; the eagerly launched time is reported beside
+    it as us_eager).  The kernel streams the
     NVFP4 weight (0.5625 bytes a weight), so the rate is weight bytes over
     time against HBM.  Weights are seeded N(0, 0.02) draws made on the
     device (the timing does not depend on their values), with enough copies
@@ -476,16 +510,19 @@ def decode_block(nv, torch, dev, workspace, steps, warmup):
                 for j in range(len(shapes)):
                     torch.matmul(acts[j], w[j].t())
 
-            t = time_ms(torch, w4a4, max(steps, 20), warmup) * 1e3
-            tb = time_ms(torch, blas, max(steps, 20), warmup) * 1e3
+            t_eager = time_ms(torch, w4a4, max(steps, 20), warmup) * 1e3
+            reps = max(3, max(steps, 20) // copies)
+            t = graph_ms(torch, w4a4, copies, reps, check=lambda: ys[-1]) * 1e3
+            tb = graph_ms(torch, blas, bf_copies, max(3, max(steps, 20) // bf_copies)) * 1e3
             gbps = wbytes / (t * 1e-6) / 1e9
             rows.append({"part": part, "tokens": tokens,
                          "shapes_nk": [list(x) for x in shapes],
                          "us": round(t, 2), "weight_gbps": round(gbps, 1),
                          "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                         "us_eager": round(t_eager, 2),
                          "hipblaslt_bf16_us": round(tb, 2), "speedup_vs_hipblaslt": round(tb / t, 3)})
-            log(f"decode {part} x{tokens}: {t:.1f} us ({gbps:.0f} GB/s of NVFP4 weight); "
-                f"hipBLASLt BF16 {tb:.1f} us; x{tb / t:.2f}")
+            log(f"decode {part} x{tokens}: {t:.1f} us ({gbps:.0f} GB/s of NVFP4 weight; "
+                f"{t_eager:.1f} us launched one by one); hipBLASLt BF16 {tb:.1f} us; x{tb / t:.2f}")
         del bf, qs, q0
         torch.cuda.empty_cache()
     return {"kernel": "w4a4_gemm_decode", "bytes_per_weight": 0.5625, "rows": rows}
