@@ -588,7 +588,8 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   // instead of being hoisted out of it (they would stay live, and spill,
   // across the main loop).
   int lane_e = lane;
-  if constexpr (kPersist) asm volatile("" : "+v"(lane_e));
+  if constexpr (kPersist)    // the lane index again, from the hardware
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
   const int fr_e = lane_e & 31, fh_e = lane_e >> 5;
   // kPersist: one output type, its bands in this tile's last slot
   uint8_t* const band_base = kPersist ? lds + slot(nk - 1) * kStageBytes : lds;
