@@ -8,9 +8,9 @@ largest tensors whole in test time, so:
 
 * alpha of every tensor is compared exactly (the oracle takes the amax of
   the full BF16 tensor);
-* codes and scale bytes are compared bit-exactly on sampled rows: the first
-  and last row, the row holding the tensor's largest magnitude, and seeded
-  random rows (all rows where the tensor is small);
+* codes and scale bytes are compared bit-exactly on every element of every
+  activation and weight tensor (the oracle runs in row slices in parallel
+  worker processes);
 * GEMM outputs are compared on a sampled row x column grid: the oracle
   quantises only those rows of each operand, with the full-tensor alpha.
 
@@ -28,6 +28,7 @@ from nvfp4_w4a4_gemm_amd import binding as nv
 from nvfp4_w4a4_gemm_amd.workloads import workload
 
 from test_gpu_parity import assert_gemm_close, host_bits
+from oracle_pool import new_pool, quantize_all_rows, quantize_many
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +36,12 @@ DEV = "cuda:0"
 ROWS = 192          # sampled rows per tensor (beyond first / last / amax row)
 GEMM_ROWS = 48      # sampled output rows per GEMM
 GEMM_COLS = 192     # sampled output columns per GEMM
+
+
+@pytest.fixture(scope="module")
+def pool():
+    with new_pool() as p:
+        yield p
 
 
 def sample(n, count, seed, must=()):
@@ -68,15 +75,16 @@ class Quantized:
         torch.cuda.synchronize()
         self.rows = sample(bits.shape[0], ROWS, seed, must=(amax_row(bits),))
 
-    def check(self):
+    def check(self, pool):
+        """alpha exact; every scale byte and code byte equal to the oracle's."""
         assert self.q.alpha.item() == float(self.alpha), (self.name, self.q.alpha.item(), self.alpha)
-        ref = orc.quantize(self.bits[self.rows], alpha=self.alpha)
-        rows_t = torch.from_numpy(self.rows).to(DEV)
-        s = self.q.scales.index_select(0, rows_t).cpu().numpy()
-        c = self.q.codes.index_select(0, rows_t).cpu().numpy()
-        bad = np.argwhere(s != ref[1])
+        ref_s, ref_c = quantize_all_rows(pool, self.bits, self.alpha)
+        s = self.q.scales.cpu().numpy()
+        c = self.q.codes.cpu().numpy()
+        assert s.shape == ref_s.shape and c.shape == ref_c.shape, self.name
+        bad = np.argwhere(s != ref_s)
         assert bad.size == 0, f"{self.name}: scale bytes differ at {bad[:4].tolist()}"
-        bad = np.argwhere(c != ref[2])
+        bad = np.argwhere(c != ref_c)
         assert bad.size == 0, f"{self.name}: code bytes differ at {bad[:4].tolist()}"
 
     def oracle_rows(self, rows):
@@ -104,18 +112,18 @@ def check_gemm(name, a, w, seed, a_rows_of_output=None, out_rows=None):
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
-def test_dense_config(cfg):
+def test_dense_config(cfg, pool):
     wl = workload(cfg)
     print(f"\n[cfg {cfg}] {wl.title}: generating", flush=True)
     acts, wts, keep = {}, {}, {}
     for i, g in enumerate(wl.gemms):
         if g.act not in acts:
             acts[g.act] = Quantized(g.act, wl.tensors[g.act].full(), False, 100 * cfg + i)
-            acts[g.act].check()
-            print(f"[cfg {cfg}] {g.act} {acts[g.act].bits.shape}: alpha and "
-                  f"{len(acts[g.act].rows)} rows of codes/scales bit-exact", flush=True)
+            acts[g.act].check(pool)
+            print(f"[cfg {cfg}] {g.act} {acts[g.act].bits.shape}: alpha and every "
+                  f"code/scale byte bit-exact", flush=True)
         wts[g.weight] = Quantized(g.weight, wl.tensors[g.weight].full(), True, 200 * cfg + i)
-        wts[g.weight].check()
+        wts[g.weight].check(pool)
         y16 = check_gemm(f"cfg {cfg} {g.name}", acts[g.act], wts[g.weight], 300 * cfg + i)
         if cfg == 4:
             # quantise-on-load: bit-identical to quantise-then-GEMM at full size
@@ -139,15 +147,15 @@ def test_dense_config(cfg):
         print("[cfg 2] Q|K|V stacked GEMM bit-identical to the three GEMMs", flush=True)
 
 
-def test_grouped_moe_config():
+def test_grouped_moe_config(pool):
     wl = workload(5)
     e_count, topk = wl.experts, wl.topk
     token_of_row, offsets = wl.routing()
     print(f"\n[cfg 5] {wl.title}: generating", flush=True)
     x = Quantized("X", wl.tensors["X"].full(), False, 501)
-    x.check()
+    x.check(pool)
     h = Quantized("H", wl.tensors["H"].full(), False, 502)
-    h.check()
+    h.check(pool)
     w_gu = [wl.tensors[f"W_gu[{e}]"].full() for e in range(e_count)]
     w_dn = [wl.tensors[f"W_down[{e}]"].full() for e in range(e_count)]
     off_t = torch.from_numpy(offsets).to(DEV)
@@ -161,6 +169,16 @@ def test_grouped_moe_config():
         b_scales = torch.stack([q.scales for q in qws])
         b_alpha = torch.cat([q.alpha for q in qws])
         del qws
+        # every expert's weight: alpha exact, every code and scale byte
+        alphas = [oracle_alpha(b) for b in wbits]
+        assert np.array_equal(b_alpha.cpu().numpy(), np.array(alphas, dtype=np.float32)), name
+        refs = quantize_many(pool, list(zip(wbits, alphas)))
+        got_s, got_c = b_scales.cpu().numpy(), b_codes.cpu().numpy()
+        for e, (rs, rc) in enumerate(refs):
+            assert rs.shape == got_s[e].shape and rc.shape == got_c[e].shape, (name, e)
+            assert np.array_equal(got_s[e], rs) and np.array_equal(got_c[e], rc), (name, e)
+        print(f"[cfg 5 {name}] all {e_count} expert weights: alpha and every code/scale byte "
+              f"bit-exact", flush=True)
         m = int(offsets[-1])
         n = wbits[0].shape[0]
         y16 = torch.empty(m, n, dtype=torch.bfloat16, device=DEV)
