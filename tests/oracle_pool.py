@@ -51,3 +51,17 @@ def quantize_many(pool, tensors):
         mine = [p for p, o in zip(parts, owner) if o == t]
         out.append((np.concatenate([p[0] for p in mine]), np.concatenate([p[1] for p in mine])))
     return out
+
+
+def _rms_slice(args):
+    bits, gamma_bits, eps = args
+    return orc.rmsnorm(bits, gamma_bits, eps)[1]
+
+
+def rmsnorm_all_rows(pool, bits: np.ndarray, gamma_bits: np.ndarray, eps):
+    """The oracle's RMSNorm (BF16 bits) of every row of bits, in row slices."""
+    rows, k = bits.shape
+    step = max(1, (1 << 20) // k)
+    parts = pool.map(_rms_slice, [(bits[r:r + step], gamma_bits, eps) for r in range(0, rows, step)],
+                     timeout=TIMEOUT_S)
+    return np.concatenate(list(parts))

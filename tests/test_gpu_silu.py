@@ -20,6 +20,7 @@ from nvfp4_w4a4_gemm_amd import binding as nv
 
 from test_gpu_parity import (assert_gemm_close, assert_quant_equal, bf16_ordered, dev_bf16,
                              host_bits, normal_bits)
+from oracle_pool import new_pool, quantize_all_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -147,9 +148,10 @@ def test_silu_mul_full_size_mlp_config():
     """The gate|up projection of the Qwen3-8B-shaped MLP configuration at
     full size (X 32768x4096 with outlier channels, gate and up 12288x4096 ~
     N(0, 0.02)), in the launch configuration the benchmark times: alpha of H
-    exact against the oracle's amax of the kernel's whole H, then sampled
-    rows of H within one BF16 ulp of the oracle's SiLU*up of the kernel's
-    float32 gate/up, and their codes and scales bit-exact."""
+    exact against the oracle's amax of the kernel's whole H, every code and
+    scale byte of H equal to the oracle's quantisation of the kernel's H, and
+    sampled rows of H within one BF16 ulp of the oracle's SiLU*up of the
+    kernel's float32 gate/up."""
     from nvfp4_w4a4_gemm_amd.workloads import workload
     from test_gpu_configs import oracle_alpha, sample
     wl = workload(3)
@@ -177,9 +179,11 @@ def test_silu_mul_full_size_mlp_config():
     hb = hb_all[rows]
     d = np.abs(bf16_ordered(hb) - bf16_ordered(h_ref))
     assert d.max() <= 1
-    ref = orc.quantize(hb, alpha=alpha)
-    rows_t = torch.from_numpy(rows).to(DEV)
-    assert np.array_equal(qh.scales.index_select(0, rows_t).cpu().numpy(), ref[1])
-    assert np.array_equal(qh.codes.index_select(0, rows_t).cpu().numpy(), ref[2])
-    print(f"[mlp gate|up] {m}x{2 * hidden}x{qa.k}: alpha of H exact, {len(rows)} rows of H "
-          f"within one ulp ({int((d > 0).sum())} off by one), their codes and scales bit-exact")
+    with new_pool() as pool:
+        ref_s, ref_c = quantize_all_rows(pool, hb_all, alpha)
+    got_s, got_c = qh.scales.cpu().numpy(), qh.codes.cpu().numpy()
+    assert got_s.shape == ref_s.shape and got_c.shape == ref_c.shape
+    assert np.array_equal(got_s, ref_s) and np.array_equal(got_c, ref_c)
+    print(f"[mlp gate|up] {m}x{2 * hidden}x{qa.k}: alpha of H exact, every code and scale "
+          f"byte of H bit-exact, {len(rows)} rows of H within one ulp "
+          f"({int((d > 0).sum())} off by one)")
