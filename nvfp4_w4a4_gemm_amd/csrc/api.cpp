@@ -206,7 +206,8 @@ nvfp4_status_t nvfp4_tensor_alpha(const void* x_bf16, int64_t M, int64_t K, int6
       nvfp4::launch_amax(static_cast<const uint16_t*>(x_bf16), M, K, ld_x, 1, w, &n_partials,
                          stream) != hipSuccess)
     return NVFP4_ERR_LAUNCH;
-  return launched(nvfp4::launch_prepare(w, n_partials, nullptr, alpha_out, w, stream));
+  return launched(nvfp4::launch_prepare(w + nvfp4::kWsPartials, n_partials, nullptr, alpha_out, w,
+                                        stream));
 }
 
 static nvfp4_status_t gemm_common(const uint8_t* a_codes, const uint8_t* a_scales,
@@ -306,6 +307,7 @@ nvfp4_status_t w4a4_gemm_silu_mul_quantize(const uint8_t* a_codes, const uint8_t
     if (!aligned(h_codes, 8)) return NVFP4_ERR_ALIGN;
     constexpr int64_t kMaxBytes = (int64_t(1) << 32) - 1;
     if (M * (K / 2) > kMaxBytes || N * (K / 2) > kMaxBytes) return NVFP4_ERR_SHAPE;
+    if (M * (nh / 16) >= kMaxDim) return NVFP4_ERR_SHAPE;     // H's blocks, as the quantiser's
   }
   if (workspace == nullptr || workspace_bytes < w4a4_gemm_silu_mul_workspace_bytes(M, N))
     return NVFP4_ERR_WORKSPACE;

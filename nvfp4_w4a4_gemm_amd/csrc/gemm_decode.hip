@@ -29,6 +29,8 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <atomic>
+
 #include <cstdlib>
 
 namespace nvfp4 {
@@ -524,11 +526,14 @@ __global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
 // column tile, and enough that none takes more than kMaxTiles tiles).
 template <int MT, int S, bool kARes>
 hipError_t launch_lds(const DecodeArgs& p, int lds_bytes, hipStream_t stream) {
-  static int cache_bytes[64], cache_wgs[64];
+  // per device: the LDS size the attribute was set for, and the workgroups
+  // that fit (host threads may race here: wgs is published before bytes)
+  static std::atomic<int> cache_bytes[64], cache_wgs[64];
   int dev = 0;
   (void)hipGetDevice(&dev);
   const int slot = dev & 63;
-  if (cache_bytes[slot] != lds_bytes) {
+  int fit;
+  if (cache_bytes[slot].load(std::memory_order_acquire) != lds_bytes) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(w4a4_decode_lds_kernel<MT, S, kARes>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess)
       return hipErrorInvalidValue;
@@ -540,11 +545,14 @@ hipError_t launch_lds(const DecodeArgs& p, int lds_bytes, hipStream_t stream) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 1)
       cus = 256;
-    cache_wgs[slot] = occ * cus;
-    cache_bytes[slot] = lds_bytes;
+    fit = occ * cus;
+    cache_wgs[slot].store(fit, std::memory_order_relaxed);
+    cache_bytes[slot].store(lds_bytes, std::memory_order_release);
+  } else {
+    fit = cache_wgs[slot].load(std::memory_order_relaxed);
   }
   const int tiles = (int)((p.N + kCols - 1) / kCols);
-  int wgs = tiles < cache_wgs[slot] ? tiles : cache_wgs[slot];
+  int wgs = tiles < fit ? tiles : fit;
   const int need = (tiles + kMaxTiles - 1) / kMaxTiles;
   if (wgs < need) wgs = need;
   hipLaunchKernelGGL((w4a4_decode_lds_kernel<MT, S, kARes>), dim3((unsigned)wgs), dim3(kThreads),

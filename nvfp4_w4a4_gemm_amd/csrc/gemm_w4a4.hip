@@ -35,6 +35,7 @@
 #include "kernels.h"
 #include "quant_block.h"
 
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
@@ -806,16 +807,16 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
 
 // Compute units of the current device (cached per device).
 int cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];         // 0: not yet known
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <int BM, int BN, bool kFused, int kRing, int kOcc, bool kSilu = false>

@@ -28,6 +28,8 @@
 #include "kernels.h"
 #include "quant_block.h"
 
+#include <atomic>
+
 namespace nvfp4 {
 
 namespace {
@@ -350,10 +352,10 @@ hipError_t launch_ch(const RmsQuantArgs& a, hipStream_t stream) {
   }
   // persistent: as many workgroups as fit at once (each copies the tables
   // once and walks several rows)
-  static int cache[64];
+  static std::atomic<int> cache[64];          // per device (0: not yet known)
   int dev = 0;
   (void)hipGetDevice(&dev);
-  int& fit = cache[dev & 63];
+  int fit = cache[dev & 63].load(std::memory_order_relaxed);
   if (fit == 0) {
     int occ = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, rmsnorm_quantize_kernel<CH, kPre>,
@@ -363,6 +365,7 @@ hipError_t launch_ch(const RmsQuantArgs& a, hipStream_t stream) {
         cus < 1)
       cus = 256;
     fit = occ * cus;
+    cache[dev & 63].store(fit, std::memory_order_relaxed);
   }
   const int grid = (int)(blocks < fit ? blocks : fit);
   hipLaunchKernelGGL((rmsnorm_quantize_kernel<CH, kPre>), dim3(grid), dim3(kThreads), 0, stream, a.x,
