@@ -533,7 +533,10 @@ def sweep(args):
 
     Per GEMM: the W4A4 kernel (BF16 out), the BF16 comparison kernel and
     torch.matmul (hipBLASLt) on the same shapes; per activation tensor: the
-    whole quantiser (amax, alpha, tables, quantize).  Inputs rotate over
+    whole quantiser (amax, alpha, tables, quantize).  Before each timing the
+    GPU runs 0.15 s of BF16 matmuls, so that the timings start from loaded
+    steady-state clocks, not from the idle left by host-side input
+    generation.  Inputs rotate over
     copies totalling at least 512 MB where a tensor is smaller, so reads come
     from HBM.  Configuration 4 also times the quantise-on-load GEMM;
     configuration 5 the grouped GEMMs (hipBLASLt as one matmul per expert).
@@ -553,12 +556,23 @@ def sweep(args):
         n = max(1, min(8, -(-(512 << 20) // bits.nbytes)))
         return [nv.to_device_bf16(np.roll(bits, r, axis=0) if r else bits, dev) for r in range(n)]
 
+    def settle():
+        # the host-side input generation leaves the GPU idle; about 0.15 s of
+        # sustained load brings its clocks back to their loaded steady state
+        a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+        t = time.perf_counter()
+        while time.perf_counter() - t < 0.15:
+            for _ in range(10):
+                a @ a
+            torch.cuda.synchronize()
+        del a
+
     for cfg in [int(c) for c in args.configs.split(",")]:
         wl = workload(cfg)
         log(f"sweep: configuration {cfg}: {wl.title}")
         out = {"config": cfg, "workload": wl.title, "gemms": [], "quantize": []}
         if cfg == 5:
-            out.update(sweep_grouped(wl, nv, torch, dev, ws, copies, reps, warm))
+            out.update(sweep_grouped(wl, nv, torch, dev, ws, copies, reps, warm, settle))
             print(json.dumps(out), flush=True)
             continue
         acts, qacts = {}, {}
@@ -569,6 +583,7 @@ def sweep(args):
             acts[g.act] = xs
             q = nv.nvfp4_quantize_act(xs[0], workspace=ws)
             qacts[g.act] = q
+            settle()
             t = time_ms(torch, lambda i: nv.nvfp4_quantize_act(xs[i % len(xs)], out=q,
                                                                workspace=ws), reps, warm)
             el = xs[0].numel()
@@ -585,6 +600,7 @@ def sweep(args):
             mm, kk, nn = xs[0].shape[0], xs[0].shape[1], w.shape[0]
             y = torch.empty(mm, nn, dtype=torch.bfloat16, device=dev)
             fl = 2.0 * mm * nn * kk
+            settle()
             t4 = time_ms(torch, lambda i: nv.w4a4_gemm(qa, qw, f32=False, y_bf16=y), reps, warm)
             tb = time_ms(torch, lambda i: nv.bf16_gemm_baseline(xs[i % len(xs)], w, f32=False),
                          reps, warm)
@@ -614,7 +630,7 @@ def sweep(args):
         torch.cuda.empty_cache()
 
 
-def sweep_grouped(wl, nv, torch, dev, ws, copies, reps, warm):
+def sweep_grouped(wl, nv, torch, dev, ws, copies, reps, warm, settle):
     """Configuration 5: quantise X once, gather by routing, grouped GEMMs."""
     token_of_row, offsets = wl.routing()
     off_t = torch.from_numpy(offsets).to(dev)
@@ -626,6 +642,7 @@ def sweep_grouped(wl, nv, torch, dev, ws, copies, reps, warm):
     for name, act, wname, gather in (("gate_up_proj", xs, "W_gu", tok_t),
                                      ("down_proj", hs, "W_down", None)):
         q = nv.nvfp4_quantize_act(act[0], workspace=ws)
+        settle()
         t = time_ms(torch, lambda i: nv.nvfp4_quantize_act(act[i % len(act)], out=q, workspace=ws),
                     reps, warm)
         el = act[0].numel()
@@ -645,6 +662,7 @@ def sweep_grouped(wl, nv, torch, dev, ws, copies, reps, warm):
         nn, kk = w.shape[1], w.shape[2]
         y = torch.empty(mm, nn, dtype=torch.bfloat16, device=dev)
         fl = 2.0 * mm * nn * kk
+        settle()
         t4 = time_ms(torch, lambda i: nv.w4a4_gemm_grouped(q, b_codes, b_scales, b_alpha, off_t,
                                                            a_row_index=gather, f32=False,
                                                            y_bf16=y), reps, warm)

@@ -132,13 +132,17 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel(
   for (; seg * kSegChunks < n; seg += nwaves) {
     const uint64_t c0 = seg * kSegChunks + lane;
     if (c0 + 192 < n) {
-      const u32x4 v0 = x[c0], v1 = x[c0 + 64], v2 = x[c0 + 128], v3 = x[c0 + 192];
+      // non-temporal: a streamed read, so the tensor does not churn L2 and MALL
+      const u32x4 v0 = __builtin_nontemporal_load(&x[c0]), v1 = __builtin_nontemporal_load(&x[c0 + 64]),
+                  v2 = __builtin_nontemporal_load(&x[c0 + 128]),
+                  v3 = __builtin_nontemporal_load(&x[c0 + 192]);
       m = pk_max_u16(m, pk_max_u16(pk_max_u16(chunk_amax_bits(v0), chunk_amax_bits(v1)),
                                    pk_max_u16(chunk_amax_bits(v2), chunk_amax_bits(v3))));
     } else {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (c0 + 64 * u < n) m = pk_max_u16(m, chunk_amax_bits(x[c0 + 64 * u]));
+        if (c0 + 64 * u < n)
+          m = pk_max_u16(m, chunk_amax_bits(__builtin_nontemporal_load(&x[c0 + 64 * u])));
     }
   }
   store_partial(max(m & 0xFFFFu, m >> 16), partials);
@@ -272,7 +276,8 @@ __global__ __launch_bounds__(kThreads) void quantize_flat_kernel(
   auto load_seg = [&](uint64_t seg, u32x4 (&v)[4]) __attribute__((always_inline)) {
     const uint64_t c0 = seg * kSegChunks + lane;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = c0 + 64 * u < n ? x[c0 + 64 * u] : u32x4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < 4; ++u)      // non-temporal, as in the amax pass
+      v[u] = c0 + 64 * u < n ? __builtin_nontemporal_load(&x[c0 + 64 * u]) : u32x4{0u, 0u, 0u, 0u};
   };
   // the first segment's loads are in flight while the tables are copied
   uint64_t seg = (uint64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);

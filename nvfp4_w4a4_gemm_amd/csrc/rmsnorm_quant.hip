@@ -50,7 +50,8 @@ __device__ __forceinline__ void load_row(const uint16_t* __restrict__ xr, int nc
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
     const int c = lane + 64 * j;
-    row.x[j] = c < nc ? p[c] : u32x4{0u, 0u, 0u, 0u};
+    // non-temporal: a streamed read, so the tensor does not churn L2 and MALL
+    row.x[j] = c < nc ? __builtin_nontemporal_load(&p[c]) : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
