@@ -295,33 +295,46 @@ __host__ __device__ constexpr int decode_ares_bytes(int M, int n_stages) {
   return decode_ares_code_bytes(M, n_stages) + (M * n_stages + 7) / 8 * 8 * kStageScales;
 }
 
-template <int MT, int S, bool kARes>
-__global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
+// kG groups of 4 waves share a workgroup's column tiles: group k computes
+// stages k, k + kG, ... of each tile (a tile's stages padded to a multiple
+// of kG; a padding stage reloads a real one and contributes nothing, its A
+// scales being masked to zero), each group with its own S / kG ring slots,
+// loads and wait counts, exactly as one 4-wave workgroup would.  Every wave
+// passes the same barriers.  For weights with few column tiles this runs kG
+// stage chains per CU instead of one.
+template <int MT, int S, bool kARes, int kG>
+__global__ __launch_bounds__(kThreads * kG) void w4a4_decode_lds_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ alpha_a, const uint8_t* __restrict__ b_codes,
     const uint8_t* __restrict__ b_scales, const float* __restrict__ alpha_b,
     const float* __restrict__ alpha_b_rows, int M, int N, int K,
     float* __restrict__ y_f32, uint16_t* __restrict__ y_bf16, int64_t ld_y) {
   static_assert(!kARes || MT == 1, "resident activations take one M-tile");
+  static_assert(S % kG == 0 && S / kG >= 2, "each group has its ring slots");
+  constexpr int kSG = S / kG;                          // ring slots of one group
+  constexpr int kAllWaves = kWaves * kG;
   constexpr int kTiles = kARes ? 1 : 1 + MT;           // B tile, then the A tiles
   // scale DMAs: 8 rows x 32 bytes of one tile each (all 64 lanes); wave w
   // takes halves w, w + 4, ...; a wave left without one reloads a valid
   // half into a slack area, so every wave counts the same loads
   constexpr int kScaleDmas = (2 * kTiles + kWaves - 1) / kWaves;
   constexpr int kStage = decode_stage_bytes(MT, kARes);
-  constexpr int kRed = kWaves * MT * 16 * 17 * 4;      // one tile's partial sums
+  constexpr int kRed = kAllWaves * MT * 16 * 17 * 4;   // one tile's partial sums
   static_assert(kRed <= S * kStage, "the reduction fits in the ring");
   // ring, then (kARes) the resident activation
   extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = wave_all & (kWaves - 1);            // wave within its group
+  const int grp = wave_all / kWaves;                   // its group (uniform)
   const int r16 = lane & 15;
   const int n_chunks = K / 32;
   const int n_stages = (K / 2 + kStageCodes - 1) / kStageCodes;
+  const int n_pad = (n_stages + kG - 1) / kG * kG;     // a tile's stages, padded
   const int64_t row_codes = K / 2, row_scales = K / 16;
   const int n_tiles = (N + kCols - 1) / kCols;
   const int my_tiles = (n_tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int total = my_tiles * n_stages;               // stages this workgroup computes
+  const int total = my_tiles * n_pad;                  // stages of this workgroup (padded)
 
   const __amdgpu_buffer_rsrc_t rbc = buffer_of(b_codes, (uint32_t)(N * row_codes));
   const __amdgpu_buffer_rsrc_t rbs = buffer_of(b_scales, (uint32_t)(N * row_scales));
@@ -351,12 +364,14 @@ __global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
     a_scale_off[d] = sc_tile[d] == 0 ? 0u
                      : (uint32_t)(a_row(sc_tile[d] - 1, sc_r[d]) * row_scales) + 4u * (lane & 7);
   }
-  // global stage g -> (column tile, stage within the tile); past the end
-  // the last stage is loaded again (into a slot nobody reads any more)
+  // global stage g -> (column tile, stage within the tile); a padding stage
+  // and, past the end, the last stage load a real stage again (into a slot
+  // whose data nobody uses)
   auto issue = [&](int g) __attribute__((always_inline)) {
     const int gc = g < total ? g : total - 1;
-    const int tile = (int)blockIdx.x + (gc / n_stages) * (int)gridDim.x;
-    const uint32_t st = (uint32_t)(gc % n_stages);
+    const int tile = (int)blockIdx.x + (gc / n_pad) * (int)gridDim.x;
+    const int sp = gc % n_pad;
+    const uint32_t st = (uint32_t)(sp < n_stages ? sp : n_stages - 1);
     const int nb0 = tile * kCols;
     uint8_t* base = lds + (g % S) * kStage;
     const int rb = nb0 + dma_row < N ? nb0 + dma_row : N - 1;
@@ -382,6 +397,7 @@ __global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
     }
   };
   constexpr int kDmaPerStage = kTiles + kScaleDmas;
+  static_assert((kSG - 1) * kDmaPerStage <= 63, "a group's loads in flight fit the wait counter");
 
   // resident activation: codes [M][n_stages * 256] (slot order as in the
   // ring), then scales [M][n_stages * 32]; 256-byte code segments and
@@ -393,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
   const int ares_scale_pitch = n_stages * kStageScales;
   if (kARes) {
     const int code_dmas = (M * n_stages + 3) / 4;      // 4 segments each
-    for (int i = wave; i < code_dmas; i += kWaves) {
+    for (int i = wave_all; i < code_dmas; i += kAllWaves) {
       const int seg = 4 * i + (lane >> 4);
       const int m = seg / n_stages < M ? seg / n_stages : M - 1;
       const int st = seg / n_stages < M ? seg % n_stages : n_stages - 1;
@@ -402,7 +418,7 @@ __global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
                 (uint32_t)(m * row_codes) + (uint32_t)st * kStageCodes + 16u * chunk);
     }
     const int scale_dmas = (M * n_stages + 7) / 8;     // 8 segments each
-    for (int i = wave; i < scale_dmas; i += kWaves) {
+    for (int i = wave_all; i < scale_dmas; i += kAllWaves) {
       const int seg = 8 * i + (lane >> 3);
       const int m = seg / n_stages < M ? seg / n_stages : M - 1;
       const int st = seg / n_stages < M ? seg % n_stages : n_stages - 1;
@@ -428,36 +444,40 @@ __global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
   const int ares_code = am * ares_code_pitch + (((q ^ am) & 15) << 4);
   const int ares_scale = ares_scale_base + am * ares_scale_pitch + 2 * q;
 
+  // the group's first kSG - 1 stages
 #pragma unroll
-  for (int g = 0; g < S - 1; ++g) issue(g);
+  for (int j = 0; j < kSG - 1; ++j) issue(grp + kG * j);
   if (kARes) {
-    // the resident activation is older than the ring's first S - 1 stages
-    __builtin_amdgcn_s_waitcnt(vm_wait((S - 1) * kDmaPerStage));
+    // the resident activation is older than the group's first kSG - 1 stages
+    __builtin_amdgcn_s_waitcnt(vm_wait((kSG - 1) * kDmaPerStage));
   }
 
-  int g = 0;
+  int g = grp;                                         // the group's next stage
 #pragma unroll
   for (int tt = 0; tt < kMaxTiles; ++tt) {
     if (tt < my_tiles) {
-      for (int st = 0; st < n_stages; ++st, ++g) {
-        // this wave's loads of stage g are done when at most S - 2 stages of
-        // loads are younger; the barrier makes every wave's part visible
-        // and frees the slot of stage g - 1 for the refill (a bare
-        // s_barrier: __syncthreads would also wait for every load in
-        // flight; the stage's LDS reads cannot move above it, since the
-        // refill loads, which write LDS, are issued between the two)
-        __builtin_amdgcn_s_waitcnt(vm_wait((S - 2) * kDmaPerStage));
+      for (int st = grp; st < n_pad; st += kG, g += kG) {
+        // this wave's loads of stage g are done when at most kSG - 2 of the
+        // group's stages of loads are younger; the barrier makes every
+        // wave's part visible and frees the slot of the group's stage
+        // g - kG for the refill (a bare s_barrier: __syncthreads would also
+        // wait for every load in flight; the stage's LDS reads cannot move
+        // above it, since the refill loads, which write LDS, are issued
+        // between the two)
+        __builtin_amdgcn_s_waitcnt(vm_wait((kSG - 2) * kDmaPerStage));
         __builtin_amdgcn_s_barrier();
-        issue(g + S - 1);
+        issue(g + S - kG);
         const uint8_t* base = lds + (g % S) * kStage;
+        // a padding stage (st >= n_stages) masks every A scale to zero
         const uint32_t mask = st * 16 + q < n_chunks ? 0xFFFFu : 0u;
+        const int st_r = st < n_stages ? st : n_stages - 1;   // resident-activation stage
         const u32x4 bc = *reinterpret_cast<const u32x4*>(base + rd_code);
         const uint32_t bs = *reinterpret_cast<const uint16_t*>(base + rd_scale);
         u32x4 ac[MT];
         uint32_t as[MT];
         if (kARes) {
-          ac[0] = *reinterpret_cast<const u32x4*>(ares + ares_code + st * kStageCodes);
-          as[0] = *reinterpret_cast<const uint16_t*>(ares + ares_scale + st * kStageScales) &
+          ac[0] = *reinterpret_cast<const u32x4*>(ares + ares_code + st_r * kStageCodes);
+          as[0] = *reinterpret_cast<const uint16_t*>(ares + ares_scale + st_r * kStageScales) &
                   (a_ok[0] ? mask : 0u);
         } else {
 #pragma unroll
@@ -497,10 +517,10 @@ __global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
       for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          red[((wave * MT + t) * 16 + 4 * (lane >> 4) + r) * 17 + r16] = acc[tt][t][r];
+          red[((wave_all * MT + t) * 16 + 4 * (lane >> 4) + r) * 17 + r16] = acc[tt][t][r];
       __syncthreads();
       const int col = ((int)blockIdx.x + tt * (int)gridDim.x) * kCols + n;
-      if (col < N) {
+      if (col < N && threadIdx.x < kThreads) {
         const float ab = alpha_b_rows != nullptr ? alpha_b_rows[col] : *alpha_b;
         const float scale = alpha_x * ab * 256.0f;
 #pragma unroll
@@ -509,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
           if (m < M) {
             float v = red[((0 * MT + t) * 16 + mr) * 17 + n];
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w) v += red[((w * MT + t) * 16 + mr) * 17 + n];
+            for (int w = 1; w < kAllWaves; ++w) v += red[((w * MT + t) * 16 + mr) * 17 + n];
             v *= scale;
             if (y_f32 != nullptr) y_f32[m * ld_y + col] = v;
             if (y_bf16 != nullptr) y_bf16[m * ld_y + col] = (uint16_t)f32_to_bf16_bits(v);
@@ -521,31 +541,43 @@ __global__ __launch_bounds__(kThreads) void w4a4_decode_lds_kernel(
   }
 }
 
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int c = cached[dev & 63].load(std::memory_order_relaxed);
+  if (c <= 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        c < 1)
+      c = 256;
+    cached[dev & 63].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
 // Launches the LDS-staged kernel with the ring (and resident activation)
 // in dynamic LDS, on as many workgroups as fit at once (at most one per
 // column tile, and enough that none takes more than kMaxTiles tiles).
-template <int MT, int S, bool kARes>
+template <int MT, int S, bool kARes, int kG>
 hipError_t launch_lds(const DecodeArgs& p, int lds_bytes, hipStream_t stream) {
   // per device: the LDS size the attribute was set for, and the workgroups
   // that fit (host threads may race here: wgs is published before bytes)
   static std::atomic<int> cache_bytes[64], cache_wgs[64];
+  const auto kernel = w4a4_decode_lds_kernel<MT, S, kARes, kG>;
   int dev = 0;
   (void)hipGetDevice(&dev);
   const int slot = dev & 63;
   int fit;
   if (cache_bytes[slot].load(std::memory_order_acquire) != lds_bytes) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(w4a4_decode_lds_kernel<MT, S, kARes>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess)
       return hipErrorInvalidValue;
-    int occ = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, w4a4_decode_lds_kernel<MT, S, kARes>,
-                                                     kThreads, lds_bytes) != hipSuccess ||
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads * kG, lds_bytes) !=
+            hipSuccess ||
         occ < 1)
       occ = 1;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus < 1)
-      cus = 256;
-    fit = occ * cus;
+    fit = occ * device_cus();
     cache_wgs[slot].store(fit, std::memory_order_relaxed);
     cache_bytes[slot].store(lds_bytes, std::memory_order_release);
   } else {
@@ -555,29 +587,48 @@ hipError_t launch_lds(const DecodeArgs& p, int lds_bytes, hipStream_t stream) {
   int wgs = tiles < fit ? tiles : fit;
   const int need = (tiles + kMaxTiles - 1) / kMaxTiles;
   if (wgs < need) wgs = need;
-  hipLaunchKernelGGL((w4a4_decode_lds_kernel<MT, S, kARes>), dim3((unsigned)wgs), dim3(kThreads),
-                     lds_bytes, stream, p.a_codes, p.a_scales, p.alpha_a, p.b_codes, p.b_scales,
-                     p.alpha_b, p.alpha_b_rows, (int)p.M, (int)p.N, (int)p.K, p.y_f32, p.y_bf16,
-                     p.ld_y);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(kThreads * kG), lds_bytes, stream,
+                     p.a_codes, p.a_scales, p.alpha_a, p.b_codes, p.b_scales, p.alpha_b,
+                     p.alpha_b_rows, (int)p.M, (int)p.N, (int)p.K, p.y_f32, p.y_bf16, p.ld_y);
   return hipGetLastError();
+}
+
+// One M-tile: kG stage groups a workgroup when the weight has too few column
+// tiles to give every CU several workgroups (4 groups up to one tile a CU,
+// 2 up to two), else one.
+template <bool kARes>
+hipError_t launch_one_mtile(const DecodeArgs& p, int n_stages, hipStream_t stream) {
+  const int tiles = (int)((p.N + kCols - 1) / kCols);
+  const int cus = device_cus();
+  const int kg = tiles <= cus ? 4 : tiles <= 2 * cus ? 2 : 1;
+  // ring stages: 4 a group with the resident activation, else 6 (one group)
+  // or 4 a group (several; 16 stages fill most of the LDS)
+  const int ares = kARes ? decode_ares_bytes((int)p.M, n_stages) : 0;
+  constexpr int kStage = decode_stage_bytes(1, kARes);
+  if (kARes) {
+    if (kg == 4) return launch_lds<1, 16, true, 4>(p, 16 * kStage + ares, stream);
+    if (kg == 2) return launch_lds<1, 8, true, 2>(p, 8 * kStage + ares, stream);
+    return launch_lds<1, 4, true, 1>(p, 4 * kStage + ares, stream);
+  }
+  if (kg == 4) return launch_lds<1, 16, false, 4>(p, 16 * kStage, stream);
+  if (kg == 2) return launch_lds<1, 8, false, 2>(p, 8 * kStage, stream);
+  return launch_lds<1, 6, false, 1>(p, 6 * kStage, stream);
 }
 
 template <int MT>
 hipError_t launch_mt(const DecodeArgs& p, hipStream_t stream) {
   const dim3 grid((unsigned)((p.N + kCols - 1) / kCols));
-  // ring depths (stages) measured best at these LDS footprints: the
-  // resident-activation kernel fits four workgroups a CU with 4 stages
-  constexpr int kS = MT == 1 ? 6 : MT == 2 ? 5 : 3;
-  constexpr int kSR = 4;
+  // ring depths (stages) measured best at these LDS footprints
+  constexpr int kS = MT == 2 ? 5 : 3;
   if (p.K % 64 == 0 && std::getenv("NVFP4_DECODE_DIRECT") == nullptr) {
     const int n_stages = (int)((p.K / 2 + kStageCodes - 1) / kStageCodes);
     if constexpr (MT == 1) {
       const int64_t ares_bytes = (p.M * n_stages + 7) / 8 * 8 * (int64_t)(kStageCodes + kStageScales);
-      if (ares_bytes <= kAResMaxBytes)
-        return launch_lds<MT, kSR, true>(
-            p, kSR * decode_stage_bytes(MT, true) + decode_ares_bytes((int)p.M, n_stages), stream);
+      if (ares_bytes <= kAResMaxBytes) return launch_one_mtile<true>(p, n_stages, stream);
+      return launch_one_mtile<false>(p, n_stages, stream);
+    } else {
+      return launch_lds<MT, kS, false, 1>(p, kS * decode_stage_bytes(MT, false), stream);
     }
-    return launch_lds<MT, kS, false>(p, kS * decode_stage_bytes(MT, false), stream);
   } else if (p.K % 32 == 0)
     hipLaunchKernelGGL((w4a4_decode_kernel<MT, true>), grid, dim3(kThreads), 0, stream,
                        p.a_codes, p.a_scales, p.alpha_a, p.b_codes, p.b_scales, p.alpha_b,

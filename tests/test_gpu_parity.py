@@ -254,12 +254,18 @@ def test_w4a4_gemm_deterministic():
 @pytest.mark.parametrize("m,n,k", [(1, 1024, 1024), (16, 200, 1408), (5, 50, 48),
                                    (64, 300, 256), (33, 17, 2816), (17, 1, 16),
                                    (1, 4096, 4096), (3, 129, 4112), (48, 96, 544),
-                                   (12, 40, 4096), (2, 2100, 1024)])
+                                   (12, 40, 4096), (2, 2100, 1024), (3, 1000, 2560),
+                                   (1, 6000, 1536), (12, 5000, 4096), (16, 9000, 512),
+                                   (14, 8400, 3072), (1, 20000, 512)])
 def test_w4a4_gemm_decode_matches_oracle(m, n, k):
     """Decode shape (M <= 64): one, two and four 16-row tiles, K with a
     half chunk at the end (K % 32 == 16), a single column, ragged N; the
     activation resident in LDS (small M x K) and staged with the weight
-    (12 x 4096); more column tiles than workgroups (2100 columns)."""
+    (12 x 4096).  One M-tile runs four stage groups a workgroup up to 256
+    column tiles, two up to 512, else one (on 256 CUs): each with the
+    activation resident and staged, with padding stages (K = 1536, 2560:
+    3 and 5 stages of 512), and more column tiles than workgroups (20000
+    columns)."""
     xb, wb = quantized_pair(m, n, k, seed=3 * m + n + k)
     qa = nv.nvfp4_quantize_act(dev_bf16(xb))
     qw = nv.nvfp4_quantize_weights(dev_bf16(wb))
