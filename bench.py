@@ -34,6 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_F16_PEAK_TFLOPS = 2500.0          # dense f16/bf16 MFMA, MI355X
+MFMA_FP4_PEAK_TFLOPS = 10100.0         # dense fp4/fp6 MFMA, MI355X (context only: the
+                                       # per-16 E4M3 scales rule out the block-scaled fp4 MFMA)
 HBM_PEAK_GBPS = 8000.0
 QUANT_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 16.0   # read BF16, write codes + scales
 AMAX_BYTES_PER_ELEM = 2.0
@@ -346,6 +348,10 @@ def main():
         },
         "gemm": {"ms_per_step": round(gemm_ms_step, 4),
                  "tflops": round(flops_step / (gemm_ms_step * 1e-3) / 1e12, 2),
+                 "frac_of_f16_mfma_peak": round(
+                     flops_step / (gemm_ms_step * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                 "frac_of_fp4_mfma_peak": round(
+                     flops_step / (gemm_ms_step * 1e-3) / 1e12 / MFMA_FP4_PEAK_TFLOPS, 4),
                  "qkv_ms": round(qkv_ms, 4), "o_ms": round(o_ms, 4),
                  "o_tflops": round(o_tflops, 2)},
         "rmsnorm_quantize": fused_norm,
