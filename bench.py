@@ -52,6 +52,20 @@ def source_hash(path):
         return hashlib.sha256(fh.read()).hexdigest()
 
 
+def stored_traffic(traffic_file=None, source=None):
+    """HBM bytes per Q|K|V launch from the committed counter record, or None
+    when there is none or the GEMM source has changed since it was taken."""
+    traffic_file = traffic_file or TRAFFIC_FILE
+    source = source or GEMM_SOURCE
+    if not os.path.exists(traffic_file):
+        return None
+    with open(traffic_file) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != source_hash(source):
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -299,11 +313,7 @@ def main():
     log("timing decode-shaped W4A4 GEMMs (w4a4_gemm_decode) against hipBLASLt BF16")
     decode = decode_block(nv, torch, dev, workspace, args.steps, args.warmup)
 
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        rec = json.load(open(TRAFFIC_FILE))
-        if rec.get("source_sha256") == source_hash(GEMM_SOURCE):
-            traffic = rec.get("bytes_per_launch")
+    traffic = stored_traffic()
 
     result = {
         "metric": "NVFP4 W4A4 GEMM TFLOP/s (% MFMA peak), quantize GB/s, speedup vs BF16",
