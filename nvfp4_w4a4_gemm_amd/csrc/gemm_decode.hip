@@ -279,8 +279,10 @@ constexpr int kMaxTiles = 8;
 // staged with every weight stage: the whole quantised activation is loaded
 // into LDS once, with the same 256-byte segments and XOR slot order, and
 // the ring carries the weight alone (half the LDS a stage, so more
-// workgroups fit on a CU).
-constexpr int kAResMaxBytes = 16 * 1024;
+// workgroups fit on a CU).  20 KB takes up to 8 token rows at K = 4096
+// (24576 x 4096 at 8 tokens: 16.4 us against 18.9 staged); 16 rows there
+// (37 KB) ran no faster resident, and 6144 x 4096 slower.
+constexpr int kAResMaxBytes = 20 * 1024;
 
 __host__ __device__ constexpr int decode_stage_bytes(int MT, bool ares) {
   return (ares ? 1 : 1 + MT) * kTileBytes + 256;
