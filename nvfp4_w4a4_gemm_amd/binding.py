@@ -134,6 +134,67 @@ def _check_bf16_2d(x: torch.Tensor, name: str):
         raise ValueError(f"{name} must have unit stride along K")
 
 
+# The library sees raw pointers only: shapes, dtypes, layouts and devices of
+# everything it reads or writes are checked here, before any call.
+
+def _check_device(t: torch.Tensor, dev, name: str):
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name} must be a CUDA tensor on {dev}")
+
+
+def _check_dense(t: torch.Tensor, dtype, shape, name: str):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
+def _check_quantized(codes: torch.Tensor, scales: torch.Tensor, rows: int, k: int, dev,
+                     name: str):
+    if k % 16 != 0:
+        raise ValueError(f"{name}: K = {k} is not a multiple of 16")
+    _check_dense(codes, torch.uint8, (rows, k // 2), name + ".codes")
+    _check_dense(scales, torch.uint8, (rows, k // 16), name + ".scales")
+    _check_device(codes, dev, name + ".codes")
+    _check_device(scales, dev, name + ".scales")
+
+
+def _check_alpha(alpha: torch.Tensor, n: int, dev, name: str):
+    if alpha.dtype != torch.float32 or alpha.numel() != n or not alpha.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of {n} element(s)")
+    _check_device(alpha, dev, name)
+
+
+def _check_tensor(q: "NVFP4Tensor", dev, name: str):
+    if q.codes.dim() != 2:
+        raise ValueError(f"{name}.codes must be 2-D")
+    _check_quantized(q.codes, q.scales, q.rows, q.k, dev, name)
+    _check_alpha(q.alpha, 1, dev, name + ".alpha")
+
+
+def _check_weight(b, dev, name: str):
+    """An NVFP4Tensor, or an NVFP4Stack with one tensor scale per row."""
+    if isinstance(b, NVFP4Stack):
+        if b.codes.dim() != 2:
+            raise ValueError(f"{name}.codes must be 2-D")
+        _check_quantized(b.codes, b.scales, b.rows, b.k, dev, name)
+        _check_alpha(b.alpha_rows, b.rows, dev, name + ".alpha_rows")
+    else:
+        _check_tensor(b, dev, name)
+
+
+def _check_outputs(y_f32, y_bf16, m: int, n: int, dev):
+    outs = [(y, dtype, name) for y, dtype, name in
+            ((y_f32, torch.float32, "y_f32"), (y_bf16, torch.bfloat16, "y_bf16")) if y is not None]
+    for y, dtype, name in outs:
+        if y.dtype != dtype or y.dim() != 2 or tuple(y.shape) != (m, n) or y.stride(1) != 1:
+            raise ValueError(f"{name} must be a {dtype} [{m}, {n}] tensor with unit column stride")
+    # one leading dimension is passed for both
+    if len(outs) == 2 and y_f32.stride(0) != y_bf16.stride(0):
+        raise ValueError("y_f32 and y_bf16 must share one row stride")
+    for y, _, name in outs:
+        _check_device(y, dev, name)
+
+
 def nvfp4_quantize_act(x: torch.Tensor, alpha_in: torch.Tensor | None = None,
                        out: NVFP4Tensor | None = None,
                        workspace: torch.Tensor | None = None) -> NVFP4Tensor:
@@ -145,6 +206,10 @@ def nvfp4_quantize_act(x: torch.Tensor, alpha_in: torch.Tensor | None = None,
         out = NVFP4Tensor(torch.empty(1, dtype=torch.float32, device=dev),
                           torch.empty(m, k // 16, dtype=torch.uint8, device=dev),
                           torch.empty(m, k // 2, dtype=torch.uint8, device=dev))
+    _check_quantized(out.codes, out.scales, m, k, dev, "out")
+    _check_alpha(out.alpha, 1, dev, "out.alpha")
+    if alpha_in is not None:
+        _check_alpha(alpha_in, 1, dev, "alpha_in")
     ws = workspace if workspace is not None else new_workspace(dev)
     _call("nvfp4_quantize_act", _ptr(x), m, k, x.stride(0), _ptr(alpha_in), _ptr(out.alpha),
           _ptr(out.codes), _ptr(out.scales), _ptr(ws), ws.numel(), _stream(dev))
@@ -167,10 +232,17 @@ def nvfp4_rmsnorm_quantize_act(x: torch.Tensor, gamma: torch.Tensor, eps: float,
         if tuple(y_out.shape) != (m, k):
             raise ValueError("y_out must be [M, K]")
     dev = x.device
+    _check_device(gamma, dev, "gamma")
+    if y_out is not None:
+        _check_device(y_out, dev, "y_out")
     if out is None:
         out = NVFP4Tensor(torch.empty(1, dtype=torch.float32, device=dev),
                           torch.empty(m, k // 16, dtype=torch.uint8, device=dev),
                           torch.empty(m, k // 2, dtype=torch.uint8, device=dev))
+    _check_quantized(out.codes, out.scales, m, k, dev, "out")
+    _check_alpha(out.alpha, 1, dev, "out.alpha")
+    if alpha_in is not None:
+        _check_alpha(alpha_in, 1, dev, "alpha_in")
     ws = workspace if workspace is not None else new_workspace(dev)
     _call("nvfp4_rmsnorm_quantize_act", _ptr(x), _ptr(gamma), m, k, x.stride(0),
           ctypes.c_float(eps), _ptr(alpha_in), _ptr(out.alpha), _ptr(out.codes),
@@ -226,7 +298,11 @@ def w4a4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, f32: bool = True, bf16: bool = Tru
     n = b.rows
     if b.k != k:
         raise ValueError("operands disagree on K")
-    y_f32, y_bf16 = _outputs(m, n, a.codes.device, f32, bf16, y_f32, y_bf16)
+    dev = a.codes.device
+    _check_tensor(a, dev, "a")
+    _check_tensor(b, dev, "b")
+    y_f32, y_bf16 = _outputs(m, n, dev, f32, bf16, y_f32, y_bf16)
+    _check_outputs(y_f32, y_bf16, m, n, dev)
     ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
     _call("w4a4_gemm", _ptr(a.codes), _ptr(a.scales), _ptr(a.alpha), _ptr(b.codes),
           _ptr(b.scales), _ptr(b.alpha), m, n, k, _ptr(y_f32), _ptr(y_bf16), ld,
@@ -270,7 +346,13 @@ def w4a4_gemm_multi(a: NVFP4Tensor, b: NVFP4Stack, f32: bool = True, bf16: bool 
     n = b.rows
     if b.k != k:
         raise ValueError("operands disagree on K")
-    y_f32, y_bf16 = _outputs(m, n, a.codes.device, f32, bf16, y_f32, y_bf16)
+    if not isinstance(b, NVFP4Stack):
+        raise ValueError("b must be an NVFP4Stack")
+    dev = a.codes.device
+    _check_tensor(a, dev, "a")
+    _check_weight(b, dev, "b")
+    y_f32, y_bf16 = _outputs(m, n, dev, f32, bf16, y_f32, y_bf16)
+    _check_outputs(y_f32, y_bf16, m, n, dev)
     ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
     _call("w4a4_gemm_multi", _ptr(a.codes), _ptr(a.scales), _ptr(a.alpha), _ptr(b.codes),
           _ptr(b.scales), _ptr(b.alpha_rows), m, n, k, _ptr(y_f32), _ptr(y_bf16), ld,
@@ -314,14 +396,24 @@ def w4a4_gemm_silu_mul_quantize(a: NVFP4Tensor, b: NVFP4Stack, h: torch.Tensor |
     n = b.rows
     if b.k != k:
         raise ValueError("operands disagree on K")
+    if not isinstance(b, NVFP4Stack):
+        raise ValueError("b must be the NVFP4Stack of interleave_gate_up")
     dev = a.codes.device
+    _check_tensor(a, dev, "a")
+    _check_weight(b, dev, "b")
     nh = n // 2
     if h is None:
         h = torch.empty(m, nh, dtype=torch.bfloat16, device=dev)
+    _check_bf16_2d(h, "h")
+    _check_device(h, dev, "h")
+    if tuple(h.shape) != (m, nh):
+        raise ValueError(f"h must be [{m}, {nh}]")
     if out is None:
         out = NVFP4Tensor(torch.empty(1, dtype=torch.float32, device=dev),
                           torch.empty(m, nh // 16, dtype=torch.uint8, device=dev),
                           torch.empty(m, nh // 2, dtype=torch.uint8, device=dev))
+    _check_quantized(out.codes, out.scales, m, nh, dev, "out")
+    _check_alpha(out.alpha, 1, dev, "out.alpha")
     ws = workspace if workspace is not None else silu_mul_workspace(m, n, dev)
     _call("w4a4_gemm_silu_mul_quantize", _ptr(a.codes), _ptr(a.scales), _ptr(a.alpha),
           _ptr(b.codes), _ptr(b.scales), _ptr(b.alpha_rows), m, n, k, _ptr(h), h.stride(0),
@@ -340,7 +432,11 @@ def w4a4_gemm_decode(a: NVFP4Tensor, b, f32: bool = True, bf16: bool = True,
     n = b.rows
     if b.k != k:
         raise ValueError("operands disagree on K")
-    y_f32, y_bf16 = _outputs(m, n, a.codes.device, f32, bf16, y_f32, y_bf16)
+    dev = a.codes.device
+    _check_tensor(a, dev, "a")
+    _check_weight(b, dev, "b")
+    y_f32, y_bf16 = _outputs(m, n, dev, f32, bf16, y_f32, y_bf16)
+    _check_outputs(y_f32, y_bf16, m, n, dev)
     ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
     stacked = isinstance(b, NVFP4Stack)
     _call("w4a4_gemm_decode", _ptr(a.codes), _ptr(a.scales), _ptr(a.alpha), _ptr(b.codes),
@@ -356,11 +452,28 @@ def w4a4_gemm_grouped(a: NVFP4Tensor, b_codes: torch.Tensor, b_scales: torch.Ten
                       f32: bool = True, bf16: bool = True,
                       y_f32: torch.Tensor | None = None, y_bf16: torch.Tensor | None = None):
     """Grouped (MoE) GEMM: b_* are [G, N, K/2], [G, N, K/16], [G] tensors."""
+    if b_codes.dim() != 3:
+        raise ValueError("b_codes must be [G, N, K/2]")
     g, n, kc = b_codes.shape
     k = kc * 2
+    if k != a.k:
+        raise ValueError("operands disagree on K")
+    dev = a.codes.device
+    _check_tensor(a, dev, "a")
+    _check_dense(b_codes, torch.uint8, (g, n, k // 2), "b_codes")
+    _check_dense(b_scales, torch.uint8, (g, n, k // 16), "b_scales")
+    _check_device(b_codes, dev, "b_codes")
+    _check_device(b_scales, dev, "b_scales")
+    _check_alpha(b_alpha, g, dev, "b_alpha")
+    _check_dense(group_offsets, torch.int64, (g + 1,), "group_offsets")
+    _check_device(group_offsets, dev, "group_offsets")
     if m is None:
         m = a_row_index.numel() if a_row_index is not None else a.rows
-    y_f32, y_bf16 = _outputs(m, n, a.codes.device, f32, bf16, y_f32, y_bf16)
+    if a_row_index is not None:
+        _check_dense(a_row_index, torch.int32, (m,), "a_row_index")
+        _check_device(a_row_index, dev, "a_row_index")
+    y_f32, y_bf16 = _outputs(m, n, dev, f32, bf16, y_f32, y_bf16)
+    _check_outputs(y_f32, y_bf16, m, n, dev)
     ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
     _call("w4a4_gemm_grouped", _ptr(a.codes), _ptr(a.scales), _ptr(a.alpha), a.rows,
           _ptr(a_row_index), _ptr(b_codes), _ptr(b_scales), _ptr(b_alpha), m, n, k, g,
@@ -377,7 +490,13 @@ def w4a4_gemm_fused_act(x: torch.Tensor, alpha_a: torch.Tensor, b: NVFP4Tensor,
     _check_bf16_2d(x, "x")
     m, k = x.shape
     n = b.rows
-    y_f32, y_bf16 = _outputs(m, n, x.device, f32, bf16, y_f32, y_bf16)
+    if b.k != k:
+        raise ValueError("operands disagree on K")
+    dev = x.device
+    _check_alpha(alpha_a, 1, dev, "alpha_a")
+    _check_tensor(b, dev, "b")
+    y_f32, y_bf16 = _outputs(m, n, dev, f32, bf16, y_f32, y_bf16)
+    _check_outputs(y_f32, y_bf16, m, n, dev)
     ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
     ws = workspace if workspace is not None else new_workspace(x.device)
     _call("w4a4_gemm_fused_act", _ptr(x), x.stride(0), _ptr(alpha_a), _ptr(b.codes),
@@ -392,8 +511,15 @@ def bf16_gemm_baseline(x: torch.Tensor, w: torch.Tensor,
     """BF16 comparison GEMM: Y = X W^T (w [N, K] or [G, N, K] with offsets)."""
     _check_bf16_2d(x, "x")
     m, k = x.shape
+    if w.dim() not in (2, 3):
+        raise ValueError("w must be [N, K] or [G, N, K]")
     g = 1 if w.dim() == 2 else w.shape[0]
     n = w.shape[-2]
+    _check_dense(w, torch.bfloat16, (n, k) if w.dim() == 2 else (g, n, k), "w")
+    _check_device(w, x.device, "w")
+    if group_offsets is not None:
+        _check_dense(group_offsets, torch.int64, (g + 1,), "group_offsets")
+        _check_device(group_offsets, x.device, "group_offsets")
     y_f32, y_bf16 = _outputs(m, n, x.device, f32, bf16, None, None)
     ld = (y_f32 if y_f32 is not None else y_bf16).stride(0)
     _call("bf16_gemm_baseline", _ptr(x), _ptr(w), m, n, k, g, _ptr(group_offsets),
