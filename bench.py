@@ -152,8 +152,9 @@ def time_ms(torch, fn, reps, warmup):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this layer is measured on one GPU; multi-GPU sharding is "
-                                   "described in DESIGN.md but not run", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this layer is measured on one GPU; a multi-GPU run "
+                                   "(data-parallel over token rows) is not implemented",
+                          "n_gpus": args.gpus}))
         sys.exit(2)
     if args.sweep:
         sweep(args)
