@@ -93,6 +93,30 @@ nvfp4_status_t nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K,
                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * nvfp4_quantize_act_noalloc - nvfp4_quantize_act without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The call allocates nothing: its scratch (amax partials, alpha's
+ * parameters and the decision tables) is a fixed 15 616-byte array in the
+ * library's device globals, one copy per device, held from the first call on
+ * that device until the process ends.  The scratch is the same size for every
+ * M and K, so the size limits are exactly those of nvfp4_quantize_act.  The
+ * first call on a device looks the array's address up (hipGetSymbolAddress)
+ * with that device current; a failure there returns NVFP4_ERR_LAUNCH.
+ *
+ * Every call on a device shares that device's array, and the array keeps the
+ * last call's contents (each call rewrites all of it that it reads): calls
+ * that overlap in time on one device race and give wrong results, so keep
+ * them in order on one stream (or order their streams).  Arguments, results
+ * and other errors as for nvfp4_quantize_act.
+ */
+nvfp4_status_t nvfp4_quantize_act_noalloc(const void* x_bf16, int64_t M, int64_t K,
+                                          int64_t ld_x, const float* alpha_in,
+                                          float* alpha_out, uint8_t* codes,
+                                          uint8_t* scales, hipStream_t stream);
+
+/*
  * nvfp4_quantize_weights - quantise a BF16 weight matrix (done once,
  * offline: paper.rainbus digest, 核心方法; same format as the activations)
  * into the GEMM's operand layout, N rows of K elements.

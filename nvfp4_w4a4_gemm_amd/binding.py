@@ -24,6 +24,8 @@ _c_size = ctypes.c_size_t
 _SIGNATURES = {
     "nvfp4_quantize_act": [_c_void, _c_i64, _c_i64, _c_i64, _c_void, _c_void, _c_void,
                            _c_void, _c_void, _c_size, _c_void],
+    "nvfp4_quantize_act_noalloc": [_c_void, _c_i64, _c_i64, _c_i64, _c_void, _c_void, _c_void,
+                                   _c_void, _c_void],
     "nvfp4_quantize_weights": [_c_void, _c_i64, _c_i64, _c_i64, _c_i64, _c_void, _c_void,
                                _c_void, _c_void, _c_size, _c_void],
     "nvfp4_rmsnorm_quantize_act": [_c_void, _c_void, _c_i64, _c_i64, _c_i64, ctypes.c_float,
@@ -213,6 +215,27 @@ def nvfp4_quantize_act(x: torch.Tensor, alpha_in: torch.Tensor | None = None,
     ws = workspace if workspace is not None else new_workspace(dev)
     _call("nvfp4_quantize_act", _ptr(x), m, k, x.stride(0), _ptr(alpha_in), _ptr(out.alpha),
           _ptr(out.codes), _ptr(out.scales), _ptr(ws), ws.numel(), _stream(dev))
+    return out
+
+
+def nvfp4_quantize_act_noalloc(x: torch.Tensor, alpha_in: torch.Tensor | None = None,
+                               out: NVFP4Tensor | None = None) -> NVFP4Tensor:
+    """nvfp4_quantize_act with the library's own per-device scratch instead of a
+    workspace (the library allocates nothing; calls on one device must not
+    overlap in time)."""
+    _check_bf16_2d(x, "x")
+    m, k = x.shape
+    dev = x.device
+    if out is None:
+        out = NVFP4Tensor(torch.empty(1, dtype=torch.float32, device=dev),
+                          torch.empty(m, k // 16, dtype=torch.uint8, device=dev),
+                          torch.empty(m, k // 2, dtype=torch.uint8, device=dev))
+    _check_quantized(out.codes, out.scales, m, k, dev, "out")
+    _check_alpha(out.alpha, 1, dev, "out.alpha")
+    if alpha_in is not None:
+        _check_alpha(alpha_in, 1, dev, "alpha_in")
+    _call("nvfp4_quantize_act_noalloc", _ptr(x), m, k, x.stride(0), _ptr(alpha_in),
+          _ptr(out.alpha), _ptr(out.codes), _ptr(out.scales), _stream(dev))
     return out
 
 

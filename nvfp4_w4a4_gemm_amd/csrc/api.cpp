@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/nvfp4_w4a4.h"
 #include "kernels.h"
@@ -51,6 +52,39 @@ nvfp4_status_t launched(hipError_t e) {
   return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 
+// Workspace of nvfp4_quantize_act_noalloc: a fixed 15 616 bytes (amax
+// partials, alpha's parameters and the two decision tables), the same for
+// every tensor size.  Each device holds its own copy of this array from the
+// module's load until the process ends; all calls on a device share it.
+static __device__ __align__(256) uint8_t scratch[kWorkspaceBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.  The array's name is a host
+// stand-in in host code; only this address may be passed to kernels.
+nvfp4_status_t scratch_address(void** out) {
+  static std::atomic<void*> addr[64];
+  static std::mutex mu;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return NVFP4_ERR_UNSUPPORTED;
+  }
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+        (void)hipGetLastError();
+        return NVFP4_ERR_LAUNCH;
+      }
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return NVFP4_OK;
+}
+
 // Common validation of a BF16 source [rows][K] with the given strides.
 nvfp4_status_t check_source(const void* x, int64_t rows, int64_t K,
                             int64_t stride_row, int64_t stride_k) {
@@ -76,20 +110,25 @@ nvfp4_status_t check_outputs(const void* y_f32, const void* y_bf16, int64_t N,
   return NVFP4_OK;
 }
 
+// use_scratch: the workspace is the device's `scratch` array (ws ignored).
 nvfp4_status_t quantize_common(const void* x, int64_t rows, int64_t K,
                                int64_t stride_row, int64_t stride_k,
                                const float* alpha_in, float* alpha_out,
                                uint8_t* codes, uint8_t* scales, void* ws,
-                               size_t ws_bytes, hipStream_t stream) {
+                               size_t ws_bytes, hipStream_t stream,
+                               bool use_scratch = false) {
   if (alpha_out == nullptr) return NVFP4_ERR_NULL;
   if (rows > 0 && (x == nullptr || codes == nullptr || scales == nullptr))
     return NVFP4_ERR_NULL;
   nvfp4_status_t st = check_source(x, rows, K, stride_row, stride_k);
   if (st != NVFP4_OK) return st;
-  if (ws == nullptr || ws_bytes < kWorkspaceBytes) return NVFP4_ERR_WORKSPACE;
-  if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
+  if (!use_scratch) {
+    if (ws == nullptr || ws_bytes < kWorkspaceBytes) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
+  }
   if (rows > 0 && !aligned(codes, 8)) return NVFP4_ERR_ALIGN;
   if ((st = check_device()) != NVFP4_OK) return st;
+  if (use_scratch && (st = scratch_address(&ws)) != NVFP4_OK) return st;
 
   uint8_t* w = static_cast<uint8_t*>(ws);
   const uint16_t* xs = static_cast<const uint16_t*>(x);
@@ -131,6 +170,14 @@ nvfp4_status_t nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K, int6
                                   hipStream_t stream) {
   return quantize_common(x_bf16, M, K, ld_x, 1, alpha_in, alpha_out, codes, scales, workspace,
                          workspace_bytes, stream);
+}
+
+nvfp4_status_t nvfp4_quantize_act_noalloc(const void* x_bf16, int64_t M, int64_t K,
+                                          int64_t ld_x, const float* alpha_in,
+                                          float* alpha_out, uint8_t* codes, uint8_t* scales,
+                                          hipStream_t stream) {
+  return quantize_common(x_bf16, M, K, ld_x, 1, alpha_in, alpha_out, codes, scales, nullptr, 0,
+                         stream, true);
 }
 
 nvfp4_status_t nvfp4_rmsnorm_quantize_act(const void* x_bf16, const void* gamma_bf16, int64_t M,

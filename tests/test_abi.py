@@ -94,6 +94,21 @@ def test_quantize_act_validation(lib):
 
 
 @needs_lib
+def test_quantize_act_noalloc_validation(lib):
+    f = lib.nvfp4_quantize_act_noalloc
+    # x, M, K, ld, alpha_in, alpha_out, codes, scales, stream (no workspace)
+    assert f(p(), 4, 32, 32, None, p(), p(), p(), None) == UNSUPPORTED
+    assert f(p(), 4, 33, 33, None, p(), p(), p(), None) == SHAPE     # K % 16
+    assert f(p(), -1, 32, 32, None, p(), p(), p(), None) == SHAPE    # M < 0
+    assert f(p(), 4, 32, 16, None, p(), p(), p(), None) == SHAPE     # ld < K
+    assert f(p(), 1 << 27, 1 << 8, 1 << 8, None, p(), p(), p(), None) == SHAPE  # blocks
+    assert f(None, 4, 32, 32, None, p(), p(), p(), None) == NULL
+    assert f(p(), 4, 32, 32, None, None, p(), p(), None) == NULL     # alpha_out
+    assert f(p(2), 4, 32, 32, None, p(), p(), p(), None) == ALIGN    # x
+    assert f(p(), 4, 32, 32, None, p(), p(4), p(), None) == ALIGN    # codes
+
+
+@needs_lib
 def test_quantize_weights_validation(lib):
     f = lib.nvfp4_quantize_weights
     # w, N, K, stride_n, stride_k, alpha_out, codes, scales, ws, ws_bytes, stream
