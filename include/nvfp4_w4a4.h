@@ -71,6 +71,27 @@ const char* nvfp4_status_string(nvfp4_status_t status);
 size_t nvfp4_workspace_bytes(void);
 
 /*
+ * Kernel-path flags: a process-wide setting (default 0) that tests and
+ * benchmarks use to reach paths the size-based choice would not take, or to
+ * stop every call at the device check.  Results do not depend on the path
+ * (each path is checked against the same bounds).  Not for production use;
+ * changing the flags while other threads launch work is allowed but those
+ * launches may use either setting.
+ *   NVFP4_PATH_GEMM_GRID       the W4A4 GEMMs launch one workgroup per tile
+ *                              instead of the persistent tile walk
+ *   NVFP4_PATH_DECODE_DIRECT   w4a4_gemm_decode uses its register-load kernel
+ *                              for every K
+ *   NVFP4_PATH_REJECT_DEVICE   every entry point that would launch work
+ *                              returns NVFP4_ERR_UNSUPPORTED after validating
+ *                              its arguments (it can only reject a device)
+ */
+#define NVFP4_PATH_GEMM_GRID 1
+#define NVFP4_PATH_DECODE_DIRECT 2
+#define NVFP4_PATH_REJECT_DEVICE 4
+void nvfp4_set_path_flags(int flags);
+int nvfp4_path_flags(void);
+
+/*
  * nvfp4_quantize_act - quantise a BF16 activation tensor X [M][K] (row
  * stride ld_x elements) to NVFP4 on the fly.
  *

@@ -53,7 +53,13 @@ _SIGNATURES = {
 }
 
 EXPORTS = sorted(list(_SIGNATURES) + ["nvfp4_status_string", "nvfp4_workspace_bytes",
-                                      "w4a4_gemm_silu_mul_workspace_bytes"])
+                                      "w4a4_gemm_silu_mul_workspace_bytes",
+                                      "nvfp4_set_path_flags", "nvfp4_path_flags"])
+
+# kernel-path flags (nvfp4_set_path_flags), for tests and benchmarks
+PATH_GEMM_GRID = 1
+PATH_DECODE_DIRECT = 2
+PATH_REJECT_DEVICE = 4
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_ALIGN",
           4: "NVFP4_ERR_UNSUPPORTED", 5: "NVFP4_ERR_LAUNCH", 6: "NVFP4_ERR_WORKSPACE"}
@@ -87,6 +93,10 @@ def lib() -> ctypes.CDLL:
         handle.nvfp4_workspace_bytes.restype = ctypes.c_size_t
         handle.w4a4_gemm_silu_mul_workspace_bytes.argtypes = [_c_i64, _c_i64]
         handle.w4a4_gemm_silu_mul_workspace_bytes.restype = ctypes.c_size_t
+        handle.nvfp4_set_path_flags.argtypes = [ctypes.c_int]
+        handle.nvfp4_set_path_flags.restype = None
+        handle.nvfp4_path_flags.argtypes = []
+        handle.nvfp4_path_flags.restype = ctypes.c_int
         _lib = handle
     return _lib
 
@@ -103,6 +113,23 @@ def _ptr(t):
 
 def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class path_flags:
+    """Context manager: run a block with the library's kernel-path flags set
+    (NVFP4_PATH_* of the C header), restoring the previous flags after."""
+
+    def __init__(self, flags: int):
+        self.flags = flags
+
+    def __enter__(self):
+        self.prev = lib().nvfp4_path_flags()
+        lib().nvfp4_set_path_flags(self.flags)
+        return self
+
+    def __exit__(self, *exc):
+        lib().nvfp4_set_path_flags(self.prev)
+        return False
 
 
 def workspace_bytes() -> int:
@@ -534,6 +561,8 @@ def bf16_gemm_baseline(x: torch.Tensor, w: torch.Tensor,
     """BF16 comparison GEMM: Y = X W^T (w [N, K] or [G, N, K] with offsets)."""
     _check_bf16_2d(x, "x")
     m, k = x.shape
+    if m > 1 and x.stride(0) != k:
+        raise ValueError("x must be row-contiguous (the BF16 GEMM takes no row stride)")
     if w.dim() not in (2, 3):
         raise ValueError("w must be [N, K] or [G, N, K]")
     g = 1 if w.dim() == 2 else w.shape[0]

@@ -4,7 +4,6 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
-#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -21,19 +20,20 @@ bool aligned(const void* p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }
 
+std::atomic<int> g_path_flags{0};
+
 // Cached per-device check that the current device is gfx950.  The cache only
-// memoises hipGetDeviceProperties; NVFP4_FORCE_ARCH overrides the detected
-// architecture name (used to exercise the unsupported-device path).
+// memoises hipGetDeviceProperties; the NVFP4_PATH_REJECT_DEVICE flag makes
+// every device fail the check (it never makes another device pass).
 nvfp4_status_t check_device() {
   static std::atomic<int> cache[64];
+  if (g_path_flags.load(std::memory_order_relaxed) & nvfp4::kPathRejectDevice)
+    return NVFP4_ERR_UNSUPPORTED;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
     (void)hipGetLastError();
     return NVFP4_ERR_UNSUPPORTED;
   }
-  const char* force = std::getenv("NVFP4_FORCE_ARCH");
-  if (force != nullptr)
-    return std::strncmp(force, "gfx950", 6) == 0 ? NVFP4_OK : NVFP4_ERR_UNSUPPORTED;
   if (dev < 64) {
     int c = cache[dev].load(std::memory_order_relaxed);
     if (c != 0) return c == 1 ? NVFP4_OK : NVFP4_ERR_UNSUPPORTED;
@@ -147,7 +147,17 @@ nvfp4_status_t quantize_common(const void* x, int64_t rows, int64_t K,
 
 }  // namespace
 
+int nvfp4::path_flags() { return g_path_flags.load(std::memory_order_relaxed); }
+
 extern "C" {
+
+void nvfp4_set_path_flags(int flags) {
+  g_path_flags.store(flags & (nvfp4::kPathGemmGrid | nvfp4::kPathDecodeDirect |
+                              nvfp4::kPathRejectDevice),
+                     std::memory_order_relaxed);
+}
+
+int nvfp4_path_flags(void) { return g_path_flags.load(std::memory_order_relaxed); }
 
 const char* nvfp4_status_string(nvfp4_status_t s) {
   switch (s) {
@@ -464,6 +474,8 @@ nvfp4_status_t w4a4_gemm_fused_act(const void* x_bf16, int64_t ld_x, const float
   if ((st = check_source(x_bf16, M, K, ld_x, 1)) != NVFP4_OK) return st;
   if (!aligned(b_codes, 16)) return NVFP4_ERR_ALIGN;
   if (K % 128 == 0 && !aligned(b_scales, 8)) return NVFP4_ERR_ALIGN;
+  // the kernel addresses the weight with 32-bit byte offsets
+  if (N * (K / 2) > (int64_t(1) << 32) - 1) return NVFP4_ERR_SHAPE;
   if (workspace == nullptr || workspace_bytes < kWorkspaceBytes) return NVFP4_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
   if ((st = check_device()) != NVFP4_OK) return st;

@@ -622,7 +622,7 @@ hipError_t launch_mt(const DecodeArgs& p, hipStream_t stream) {
   const dim3 grid((unsigned)((p.N + kCols - 1) / kCols));
   // ring depths (stages) measured best at these LDS footprints
   constexpr int kS = MT == 2 ? 5 : 3;
-  if (p.K % 64 == 0 && std::getenv("NVFP4_DECODE_DIRECT") == nullptr) {
+  if (p.K % 64 == 0 && (path_flags() & kPathDecodeDirect) == 0) {
     const int n_stages = (int)((p.K / 2 + kStageCodes - 1) / kStageCodes);
     if constexpr (MT == 1) {
       const int64_t ares_bytes = (p.M * n_stages + 7) / 8 * 8 * (int64_t)(kStageCodes + kStageScales);

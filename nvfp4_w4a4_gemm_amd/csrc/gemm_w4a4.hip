@@ -36,8 +36,6 @@
 #include "quant_block.h"
 
 #include <atomic>
-#include <cstdlib>
-#include <cstring>
 #include <type_traits>
 
 namespace nvfp4 {
@@ -786,11 +784,58 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
         __builtin_amdgcn_wave_barrier();
       }
   };
+  // Interior tiles with 16-byte rows: the read-back of band q is issued,
+  // then band q + 1 is formed and written over it (a wave's LDS operations
+  // complete in order, so the writes land after the reads), then band q is
+  // stored; the work of band q + 1 hides the latency of band q's reads.
+  auto band_read = [&](auto tag, const uint8_t* band, u32x4* v) __attribute__((always_inline)) {
+    constexpr int kE = (int)sizeof(decltype(tag)), kPitch = kE == 4 ? kPitch32 : kPitch16;
+    constexpr int kPer = 16 / kE, kLanesPerRow = WN / kPer, kRowsPerQ = 64 / kLanesPerRow;
+    constexpr int kQ = kBandRows / kRowsPerQ;
+    const int lane_row = lane_e / kLanesPerRow, lane_col = (lane_e % kLanesPerRow) * kPer;
+    const uint8_t* src = band + lane_row * kPitch + lane_col * kE;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) v[q] = *reinterpret_cast<const u32x4*>(src + q * kRowsPerQ * kPitch);
+  };
+  auto band_put = [&](auto* y, const u32x4* v, int i, int h) __attribute__((always_inline)) {
+    using T = typename std::remove_pointer<decltype(y)>::type;
+    constexpr int kE = (int)sizeof(T);
+    constexpr int kPer = 16 / kE, kLanesPerRow = WN / kPer, kRowsPerQ = 64 / kLanesPerRow;
+    constexpr int kQ = kBandRows / kRowsPerQ;
+    const int lane_row = lane_e / kLanesPerRow, lane_col = (lane_e % kLanesPerRow) * kPer;
+    const int64_t row0 = tc.m0 + wm + 32 * i + kBandRows * h;
+    T* dst = y + (row0 + lane_row) * p.ld_y + tc.n0 + wn + lane_col;
+    const int64_t step = (int64_t)kRowsPerQ * p.ld_y;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+      __builtin_nontemporal_store(v[q], reinterpret_cast<u32x4*>(dst + q * step));
+  };
+  auto epilogue_piped = [&](auto k32, auto k16) __attribute__((always_inline)) {
+    u32x4 v32[8], v16[4];
+    band_write(0, 0, k32, k16);
+#pragma unroll
+    for (int q = 0; q < 2 * TM; ++q) {
+      __builtin_amdgcn_wave_barrier();
+      if (decltype(k32)::value) band_read(float{}, band32, v32);
+      if (decltype(k16)::value) band_read(uint16_t{}, band16, v16);
+      if (q + 1 < 2 * TM) band_write((q + 1) >> 1, (q + 1) & 1, k32, k16);
+      __builtin_amdgcn_wave_barrier();
+      if (decltype(k32)::value) band_put(p.y_f32, v32, q >> 1, q & 1);
+      if (decltype(k16)::value) band_put(reinterpret_cast<__bf16*>(p.y_bf16), v16, q >> 1, q & 1);
+    }
+  };
   using yes = std::true_type;
   using no = std::false_type;
-  if (want32 && want16) epilogue(yes{}, yes{});
-  else if (want32) epilogue(yes{}, no{});
-  else epilogue(no{}, yes{});
+  const bool piped = interior && (!want32 || p.vec_f32) && (!want16 || p.vec_bf16);
+  if (piped) {
+    if (want32 && want16) epilogue_piped(yes{}, yes{});
+    else if (want32) epilogue_piped(yes{}, no{});
+    else epilogue_piped(no{}, yes{});
+  } else {
+    if (want32 && want16) epilogue(yes{}, yes{});
+    else if (want32) epilogue(yes{}, no{});
+    else epilogue(no{}, yes{});
+  }
   }
 
   if (!has_next) break;
@@ -826,10 +871,9 @@ hipError_t launch_tiles(const W4A4Args& a, hipStream_t stream) {
   const int tiles_n = (int)((a.N + BN - 1) / BN);
   // persistent walk: the DMA path with a 4-deep ring, dense, one output type
   // (its bands fit one ring slot), at least 4 stages and two tiles per CU;
-  // NVFP4_GEMM_PERSIST=0 turns it off
+  // the NVFP4_PATH_GEMM_GRID flag turns it off
   if constexpr (kRing == 4 && !kFused) {
-    const char* env = std::getenv("NVFP4_GEMM_PERSIST");
-    const bool allowed = env == nullptr || std::strcmp(env, "0") != 0;
+    const bool allowed = (path_flags() & kPathGemmGrid) == 0;
     const int64_t n_tiles = (int64_t)tiles_m * tiles_n;
     const int cus = cu_count();
     if (allowed && a.K % kBK == 0 && a.K / kBK >= 4 && a.group_offsets == nullptr &&
@@ -850,13 +894,9 @@ hipError_t launch_tiles(const W4A4Args& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile choice: NVFP4_GEMM_TILE (256x256, 128x256, 128x128) overrides the
-// size-based default, for tuning.  0: 256x256, 1: 128x256, 2: 128x128.
+// Tile choice: 256x256 when that gives at least one tile per CU of the
+// chip, else 128x128.  0: 256x256, 1: 128x256, 2: 128x128.
 int tile_choice(int64_t M, int64_t N) {
-  const char* env = std::getenv("NVFP4_GEMM_TILE");
-  if (env != nullptr && std::strcmp(env, "256x256") == 0) return 0;
-  if (env != nullptr && std::strcmp(env, "128x256") == 0) return 1;
-  if (env != nullptr && std::strcmp(env, "128x128") == 0) return 2;
   const int64_t t0 = ((M + 255) / 256) * ((N + 255) / 256);
   return t0 >= 256 ? 0 : 2;
 }

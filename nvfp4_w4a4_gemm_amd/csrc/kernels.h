@@ -7,6 +7,10 @@
 
 namespace nvfp4 {
 
+// Kernel-path flags set through nvfp4_set_path_flags (api.cpp).
+constexpr int kPathGemmGrid = 1, kPathDecodeDirect = 2, kPathRejectDevice = 4;
+int path_flags();
+
 // ---- quantiser workspace layout (bytes) ------------------------------------
 constexpr int kAmaxPartials = 1024;          // per-workgroup maxima (uint32)
 constexpr size_t kWsPartials = 0;

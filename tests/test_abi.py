@@ -2,7 +2,7 @@
 and rejects bad arguments before launching anything.
 
 These tests make no compute calls.  Calls with otherwise valid arguments run
-with NVFP4_FORCE_ARCH set to a non-gfx950 name, so the library stops at the
+under the NVFP4_PATH_REJECT_DEVICE path flag, so the library stops at the
 device check (NVFP4_ERR_UNSUPPORTED) on any machine, GPU or not.
 """
 import ctypes
@@ -53,10 +53,10 @@ def test_binding_signatures_cover_the_header():
 
 
 @pytest.fixture
-def lib(monkeypatch):
-    monkeypatch.setenv("NVFP4_FORCE_ARCH", "gfx942")
+def lib():
     from nvfp4_w4a4_gemm_amd import binding
-    return binding.lib()
+    with binding.path_flags(binding.PATH_REJECT_DEVICE):
+        yield binding.lib()
 
 
 FAKE = 0x10000          # 64 KiB-aligned fake device address (never dereferenced)

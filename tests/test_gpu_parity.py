@@ -275,17 +275,18 @@ def test_w4a4_gemm_decode_matches_oracle(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (20, 64, 2816), (64, 33, 512)])
-def test_w4a4_gemm_decode_direct_path(monkeypatch, m, n, k):
+def test_w4a4_gemm_decode_direct_path(m, n, k):
     """The register-load decode kernel (taken when K % 64 != 0) on shapes the
-    LDS-staged one would take, forced by NVFP4_DECODE_DIRECT: both agree with
-    the oracle."""
+    LDS-staged one would take, forced by the NVFP4_PATH_DECODE_DIRECT path
+    flag: both agree with the oracle."""
     xb, wb = quantized_pair(m, n, k, seed=5 * m + n + k)
     qa = nv.nvfp4_quantize_act(dev_bf16(xb))
     qw = nv.nvfp4_quantize_weights(dev_bf16(wb))
     y, bound, y16_ref = orc.w4a4_reference(orc.quantize(xb), orc.quantize(wb))
     s32, s16 = nv.w4a4_gemm_decode(qa, qw)
-    monkeypatch.setenv("NVFP4_DECODE_DIRECT", "1")
-    d32, d16 = nv.w4a4_gemm_decode(qa, qw)
+    with nv.path_flags(nv.PATH_DECODE_DIRECT):
+        d32, d16 = nv.w4a4_gemm_decode(qa, qw)
+        torch.cuda.synchronize()
     assert_gemm_close(s32, s16, y, bound, y16_ref)
     assert_gemm_close(d32, d16, y, bound, y16_ref)
 
@@ -406,26 +407,23 @@ def test_bf16_baseline_grouped():
 # output type): the same bits as one workgroup per tile
 # ---------------------------------------------------------------------------
 
-def _with_persist(monkeypatch, on, fn):
-    if on:
-        monkeypatch.delenv("NVFP4_GEMM_PERSIST", raising=False)
-    else:
-        monkeypatch.setenv("NVFP4_GEMM_PERSIST", "0")
-    out = fn()
-    torch.cuda.synchronize()
+def _with_persist(on, fn):
+    with nv.path_flags(0 if on else nv.PATH_GEMM_GRID):
+        out = fn()
+        torch.cuda.synchronize()
     return out
 
 
 @pytest.mark.parametrize("m,n,k,out", [(8192, 4096, 512, "bf16"), (8000, 4100, 512, "f32"),
                                        (4096, 8448, 640, "bf16")])
-def test_w4a4_gemm_persistent_equals_grid(monkeypatch, m, n, k, out):
+def test_w4a4_gemm_persistent_equals_grid(m, n, k, out):
     xb, wb = quantized_pair(m, n, k, seed=m + n + k + 3)
     qa = nv.nvfp4_quantize_act(dev_bf16(xb))
     qw = nv.nvfp4_quantize_weights(dev_bf16(wb))
     f32, bf16 = out == "f32", out == "bf16"
     run = lambda: nv.w4a4_gemm(qa, qw, f32=f32, bf16=bf16)
-    y_p = _with_persist(monkeypatch, True, run)
-    y_g = _with_persist(monkeypatch, False, run)
+    y_p = _with_persist(True, run)
+    y_g = _with_persist(False, run)
     got, ref = (y_p[0], y_g[0]) if f32 else (y_p[1].view(torch.int16), y_g[1].view(torch.int16))
     assert torch.equal(got, ref)
     rows = np.array([0, 1, 255, 256, m // 2 + 7, m - 1])
@@ -437,13 +435,13 @@ def test_w4a4_gemm_persistent_equals_grid(monkeypatch, m, n, k, out):
         assert_gemm_close(None, y_p[1][rows], y, bound, y16_ref)
 
 
-def test_w4a4_gemm_multi_persistent_equals_grid(monkeypatch):
+def test_w4a4_gemm_multi_persistent_equals_grid():
     m, k = 8192, 512
     parts = [normal_bits(n, k, seed=90 + i, std=std, outliers=False)
              for i, (n, std) in enumerate(((4096, 0.02), (1024, 0.5), (1024, 3.0)))]
     qa = nv.nvfp4_quantize_act(dev_bf16(normal_bits(m, k, seed=89)))
     stack = nv.stack_tensors([nv.nvfp4_quantize_weights(dev_bf16(w)) for w in parts])
     run = lambda: nv.w4a4_gemm_multi(qa, stack, f32=False)[1]
-    y_p = _with_persist(monkeypatch, True, run)
-    y_g = _with_persist(monkeypatch, False, run)
+    y_p = _with_persist(True, run)
+    y_g = _with_persist(False, run)
     assert torch.equal(y_p.view(torch.int16), y_g.view(torch.int16))

@@ -112,7 +112,7 @@ def test_silu_mul_empty_rows():
     assert h.shape == (0, hidden) and qh.alpha.item() == 0.0
 
 
-def test_silu_mul_persistent_equals_grid(monkeypatch):
+def test_silu_mul_persistent_equals_grid():
     """4096 tokens, hidden 4096: 512 tiles of 256 x 256, so the persistent
     tile walk runs; H, alpha, codes and scales equal the one-workgroup-per-
     tile launch bit for bit."""
@@ -123,12 +123,9 @@ def test_silu_mul_persistent_equals_grid(monkeypatch):
     stack = nv.interleave_gate_up(qg, qu)
     res = []
     for on in (True, False):
-        if on:
-            monkeypatch.delenv("NVFP4_GEMM_PERSIST", raising=False)
-        else:
-            monkeypatch.setenv("NVFP4_GEMM_PERSIST", "0")
-        q, h = nv.w4a4_gemm_silu_mul_quantize(qa, stack)
-        torch.cuda.synchronize()
+        with nv.path_flags(0 if on else nv.PATH_GEMM_GRID):
+            q, h = nv.w4a4_gemm_silu_mul_quantize(qa, stack)
+            torch.cuda.synchronize()
         res.append((q, h))
     (q1, h1), (q2, h2) = res
     assert torch.equal(h1.view(torch.int16), h2.view(torch.int16))
