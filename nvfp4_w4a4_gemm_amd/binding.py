@@ -559,10 +559,10 @@ def bf16_gemm_baseline(x: torch.Tensor, w: torch.Tensor,
                        group_offsets: torch.Tensor | None = None,
                        f32: bool = True, bf16: bool = True):
     """BF16 comparison GEMM: Y = X W^T (w [N, K] or [G, N, K] with offsets)."""
+    if x.dim() == 2 and x.shape[0] > 1 and x.stride(0) != x.shape[1]:
+        raise ValueError("x must be row-contiguous (the BF16 GEMM takes no row stride)")
     _check_bf16_2d(x, "x")
     m, k = x.shape
-    if m > 1 and x.stride(0) != k:
-        raise ValueError("x must be row-contiguous (the BF16 GEMM takes no row stride)")
     if w.dim() not in (2, 3):
         raise ValueError("w must be [N, K] or [G, N, K]")
     g = 1 if w.dim() == 2 else w.shape[0]

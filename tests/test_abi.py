@@ -109,6 +109,17 @@ def test_quantize_act_noalloc_validation(lib):
 
 
 @needs_lib
+def test_fused_gemm_rejects_weights_beyond_32_bit_offsets(lib):
+    f = lib.w4a4_gemm_fused_act
+    # x, ld_x, alpha_a, b_codes, b_scales, alpha_b, M, N, K, y32, y16, ld_y, ws, ws_bytes, stream
+    ok = [p(), 256, p(), p(), p(), p(), 16, 64, 256, None, p(), 1 << 20, p(), WS, None]
+    assert f(*ok) == UNSUPPORTED
+    big = list(ok); big[7] = 1 << 20; big[8] = 1 << 13       # N * K / 2 = 2^32 bytes
+    big[1] = 1 << 13
+    assert f(*big) == SHAPE
+
+
+@needs_lib
 def test_quantize_weights_validation(lib):
     f = lib.nvfp4_quantize_weights
     # w, N, K, stride_n, stride_k, alpha_out, codes, scales, ws, ws_bytes, stream

@@ -68,3 +68,12 @@ def test_device_arguments_are_checked():
     y32, y16 = nv.w4a4_gemm(a, b)              # well formed: runs
     torch.cuda.synchronize()
     assert torch.all(y32 == 0) and torch.all(y16 == 0)
+
+
+def test_bf16_baseline_rejects_row_strided_activations():
+    # the library's BF16 GEMM takes no row stride: a column slice of a wider
+    # tensor would be read with the wrong pitch
+    big = torch.zeros(8, 96, dtype=torch.bfloat16)
+    w = torch.zeros(16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="row-contiguous"):
+        nv.bf16_gemm_baseline(big[:, :64], w)
