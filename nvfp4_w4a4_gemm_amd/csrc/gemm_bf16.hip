@@ -1,11 +1,12 @@
 // BF16 comparison GEMM for gfx950: Y = X . W^T with BF16 operands and float32
 // accumulation.  The pages measure NVFP4 prefill against a BF16 baseline
 // ("Mix-Quant：面向智能体LLM的量化预填充与精确解码", paper.rainbus.top
-// digest, 实验结果 (3), Figure 4); this kernel is that baseline for the same
-// layer shapes, built on the same skeleton as the W4A4 kernel (256-thread
-// workgroups of 2 x 2 waves, 32x32x16 MFMAs, global -> registers -> LDS
-// double buffering, one barrier a stage), so that the comparison isolates the
-// operand format.  Each stage covers BK K-elements: lanes 0-31 of a fragment
+// digest, 实验结果 (3), Figure 4); this kernel is a plain BF16 GEMM for the
+// same layer shapes: 256-thread workgroups of 2 x 2 waves and 32x32x16 MFMAs
+// like the W4A4 kernel, but global -> registers -> LDS double buffering with a
+// full barrier a stage, none of the W4A4 kernel's LDS DMA ring, swizzle or
+// banded epilogue.  It runs well below hipBLASLt, which is the BF16 figure the
+// W4A4 layer is compared with.  Each stage covers BK K-elements: lanes 0-31 of a fragment
 // read K-elements [0, BK/2) of the stage and lanes 32-63 read [BK/2, BK),
 // eight per MFMA step.
 #include "device_common.h"
