@@ -784,58 +784,11 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
         __builtin_amdgcn_wave_barrier();
       }
   };
-  // Interior tiles with 16-byte rows: the read-back of band q is issued,
-  // then band q + 1 is formed and written over it (a wave's LDS operations
-  // complete in order, so the writes land after the reads), then band q is
-  // stored; the work of band q + 1 hides the latency of band q's reads.
-  auto band_read = [&](auto tag, const uint8_t* band, u32x4* v) __attribute__((always_inline)) {
-    constexpr int kE = (int)sizeof(decltype(tag)), kPitch = kE == 4 ? kPitch32 : kPitch16;
-    constexpr int kPer = 16 / kE, kLanesPerRow = WN / kPer, kRowsPerQ = 64 / kLanesPerRow;
-    constexpr int kQ = kBandRows / kRowsPerQ;
-    const int lane_row = lane_e / kLanesPerRow, lane_col = (lane_e % kLanesPerRow) * kPer;
-    const uint8_t* src = band + lane_row * kPitch + lane_col * kE;
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) v[q] = *reinterpret_cast<const u32x4*>(src + q * kRowsPerQ * kPitch);
-  };
-  auto band_put = [&](auto* y, const u32x4* v, int i, int h) __attribute__((always_inline)) {
-    using T = typename std::remove_pointer<decltype(y)>::type;
-    constexpr int kE = (int)sizeof(T);
-    constexpr int kPer = 16 / kE, kLanesPerRow = WN / kPer, kRowsPerQ = 64 / kLanesPerRow;
-    constexpr int kQ = kBandRows / kRowsPerQ;
-    const int lane_row = lane_e / kLanesPerRow, lane_col = (lane_e % kLanesPerRow) * kPer;
-    const int64_t row0 = tc.m0 + wm + 32 * i + kBandRows * h;
-    T* dst = y + (row0 + lane_row) * p.ld_y + tc.n0 + wn + lane_col;
-    const int64_t step = (int64_t)kRowsPerQ * p.ld_y;
-#pragma unroll
-    for (int q = 0; q < kQ; ++q)
-      __builtin_nontemporal_store(v[q], reinterpret_cast<u32x4*>(dst + q * step));
-  };
-  auto epilogue_piped = [&](auto k32, auto k16) __attribute__((always_inline)) {
-    u32x4 v32[8], v16[4];
-    band_write(0, 0, k32, k16);
-#pragma unroll
-    for (int q = 0; q < 2 * TM; ++q) {
-      __builtin_amdgcn_wave_barrier();
-      if (decltype(k32)::value) band_read(float{}, band32, v32);
-      if (decltype(k16)::value) band_read(uint16_t{}, band16, v16);
-      if (q + 1 < 2 * TM) band_write((q + 1) >> 1, (q + 1) & 1, k32, k16);
-      __builtin_amdgcn_wave_barrier();
-      if (decltype(k32)::value) band_put(p.y_f32, v32, q >> 1, q & 1);
-      if (decltype(k16)::value) band_put(reinterpret_cast<__bf16*>(p.y_bf16), v16, q >> 1, q & 1);
-    }
-  };
   using yes = std::true_type;
   using no = std::false_type;
-  const bool piped = interior && (!want32 || p.vec_f32) && (!want16 || p.vec_bf16);
-  if (piped) {
-    if (want32 && want16) epilogue_piped(yes{}, yes{});
-    else if (want32) epilogue_piped(yes{}, no{});
-    else epilogue_piped(no{}, yes{});
-  } else {
-    if (want32 && want16) epilogue(yes{}, yes{});
-    else if (want32) epilogue(yes{}, no{});
-    else epilogue(no{}, yes{});
-  }
+  if (want32 && want16) epilogue(yes{}, yes{});
+  else if (want32) epilogue(yes{}, no{});
+  else epilogue(no{}, yes{});
   }
 
   if (!has_next) break;
