@@ -76,9 +76,13 @@ def assert_gemm_close(y32, y16, y_ref, bound, y16_ref):
         val = (g16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         far = d > 1
         if far.any():
+            n_far = int(far.sum())
             assert np.all(np.abs(val - y_ref)[far] <= tol[far]), \
                 f"BF16 outputs off by {d.max()} ulp outside the float32 tolerance"
-            print(f"[bf16] {int(far.sum())} of {far.size} outputs beyond 1 ulp, "
+            # the exemption covers outputs that nearly cancel: rare, and bounded
+            assert n_far <= max(1, int(1e-4 * far.size)), \
+                f"{n_far} of {far.size} BF16 outputs beyond 1 ulp (more than 1e-4 of them)"
+            print(f"[bf16] {n_far} of {far.size} outputs beyond 1 ulp, "
                   f"all within the float32 tolerance (cancellation)")
         if y32 is not None:
             u = y32.cpu().numpy().view(np.uint32)

@@ -1,15 +1,18 @@
 """The gate|up W4A4 GEMM with SiLU(gate) * up and the next quantiser fused in
 (w4a4_gemm_silu_mul_quantize) against the oracle.
 
-The fused kernel shares the GEMM's main loop with w4a4_gemm_multi, so its
-float32 gate and up values are those w4a4_gemm_multi writes for the same
-interleaved weight; those are checked against the oracle GEMM as any W4A4
-output.  H is compared with the oracle's gated activation (reading R17,
-float64, one BF16 rounding) of those values: equal or adjacent BF16 values
-(the kernel's float32 exp and divide can put H on the other side of a BF16
-midpoint).  The quantisation of H is compared bit for bit: alpha (from the
-kernel's per-tile maxima), scale bytes and codes equal the oracle's
-quantisation of the kernel's own H.
+Two checks of H, one of which assumes nothing about the fused kernel's
+internals:
+  - end to end: H against SiLU(g) u of the exact oracle gate and up, within
+    the GEMM tolerance carried through SiLU (|d SiLU/dg| <= 1.1 everywhere)
+    plus one BF16 ulp for H's own rounding;
+  - tighter: the fused kernel shares the GEMM's main loop with
+    w4a4_gemm_multi, so H is within one BF16 ulp of the oracle's gated
+    activation (reading R17, float64, one BF16 rounding) of the float32 gate
+    and up that w4a4_gemm_multi writes for the same interleaved weight.
+The quantisation of H is compared bit for bit: alpha (from the kernel's
+per-tile maxima), scale bytes and codes equal the oracle's quantisation of
+the kernel's own H.
 """
 import numpy as np
 import pytest
@@ -25,6 +28,29 @@ from oracle_pool import new_pool, quantize_all_rows
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
+
+
+SILU_SLOPE = 1.1   # max over g of |d SiLU(g) / dg| (about 1.0998, near g = 2.40)
+
+
+def assert_h_near_exact(hb, g_ref, u_ref, tol_g, tol_u):
+    """H (BF16 bits) against SiLU(g) u of the exact gate and up values, where
+    the kernel's own g and u may differ from them by up to tol_g and tol_u
+    (the GEMM tolerance): |dH| <= (|u| + tol_u) 1.1 tol_g + (|SiLU(g)| +
+    1.1 tol_g) tol_u, plus one BF16 ulp of H (its rounding and the float32
+    arithmetic of SiLU, about 2^-17 relative)."""
+    g = np.asarray(g_ref, dtype=np.float64)
+    u = np.asarray(u_ref, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        silu = g / (1.0 + np.exp(-g))
+    exact = silu * u
+    h = orc.bf16_to_f64(hb)
+    bound = ((np.abs(u) + tol_u) * SILU_SLOPE * tol_g + (np.abs(silu) + SILU_SLOPE * tol_g) * tol_u
+             + 2.0 ** -7 * np.maximum(np.abs(h), np.abs(exact)) + 1e-30)
+    err = np.abs(h - exact)
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, f"{bad.shape[0]} H values outside the propagated bound, e.g. " \
+        f"{bad[0].tolist()}: {h[tuple(bad[0])]} vs {exact[tuple(bad[0])]}"
 
 
 def gate_up_columns(hidden):
@@ -48,13 +74,17 @@ def run_case(m, hidden, k, seed, gate_std=0.02, up_std=0.02, check_gemm=False):
     gcol, ucol = gate_up_columns(hidden)
     y = y32.cpu().numpy()
     g, u = y[:, gcol], y[:, ucol]
+    hb = host_bits(h)
     if check_gemm:
         ra = orc.quantize(xb)
+        exact = []
         for w, part in ((gb, g), (ub, u)):
             ref, bound, ref16 = orc.w4a4_reference(ra, orc.quantize(w))
             assert_gemm_close(torch.from_numpy(part), None, ref, bound, ref16)
+            exact.append((ref, 1e-4 * bound + 1e-6))
+        (g_ref, tol_g), (u_ref, tol_u) = exact
+        assert_h_near_exact(hb, g_ref, u_ref, tol_g, tol_u)
     _, h_ref = orc.silu_mul(g, u)
-    hb = host_bits(h)
     diff = np.abs(bf16_ordered(hb) - bf16_ordered(h_ref))
     assert diff.max(initial=0) <= 1, f"H off by {diff.max()} BF16 ulps at " \
         f"{np.unravel_index(diff.argmax(), diff.shape)}"
@@ -77,7 +107,7 @@ def test_silu_mul_large_tile_path():
 def test_silu_mul_saturating_gate():
     """Gate values far into both tails of SiLU (exp(-g) overflows float32
     for g < -88.7) and up values of both signs."""
-    g, hb = run_case(200, 256, 512, seed=9, gate_std=2.0, up_std=0.5)
+    g, hb = run_case(200, 256, 512, seed=9, gate_std=2.0, up_std=0.5, check_gemm=True)
     assert g.min() < -90 and g.max() > 90
     h = orc.bf16_to_f64(hb)
     assert np.all(h[g < -120] == 0)
@@ -177,6 +207,18 @@ def test_silu_mul_full_size_mlp_config():
     d = np.abs(bf16_ordered(hb) - bf16_ordered(h_ref))
     assert d.max() <= 1
     with new_pool() as pool:
+        # end to end on 16 of the sampled rows: the exact oracle gate and up
+        ra = orc.quantize(wl.tensors["X"].rows_of(rows[:16]),
+                          alpha=oracle_alpha(wl.tensors["X"].full()))
+        exact = []
+        for name in ("W_gate", "W_up"):
+            wb = wl.tensors[name].full()
+            aw = oracle_alpha(wb)
+            ws, wc = quantize_all_rows(pool, wb, aw)
+            ref, bound, _ = orc.w4a4_reference(ra, (aw, ws, wc))
+            exact.append((ref, 1e-4 * bound + 1e-6))
+        (g_ref, tol_g), (u_ref, tol_u) = exact
+        assert_h_near_exact(hb[:16], g_ref, u_ref, tol_g, tol_u)
         ref_s, ref_c = quantize_all_rows(pool, hb_all, alpha)
     got_s, got_c = qh.scales.cpu().numpy(), qh.codes.cpu().numpy()
     assert got_s.shape == ref_s.shape and got_c.shape == ref_c.shape
