@@ -60,7 +60,7 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, void* lds, uint3
       rs, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
 }
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 // s_waitcnt immediate (gfx9 encoding): vector-memory count n, no expcnt
 // wait, LDS/scalar count 0.
@@ -387,59 +387,74 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
 
   // Raw fragments of one stage in two halves (code words of steps 0-3 and
   // of steps 4-7), the scale bytes, and two sets of decoded operands: step
-  // s+1 is decoded while the MFMAs of step s issue.
-  // (the next stage's scale bytes go to asn/bsn: this stage's steps 4-7
-  // still decode with asc/bsc after the next stage's first half is read)
-  u32x4 ac0[TM], ac1[TM], bc0[TN], bc1[TN];
-  uint32_t asc[TM], bsc[TN], asn[TM], bsn[TN];
+  // s+1 is decoded while the MFMAs of step s issue.  The second halves and
+  // the scales have two sets each, for even and odd stages: the next
+  // stage's are read while this stage's steps 4-7 still decode with its own.
+  struct Half1 {
+    u32x4 a[TM], b[TN];
+  };
+  struct Scales {
+    uint32_t a[TM], b[TN];
+  };
+  u32x4 ac0[TM], bc0[TN];
+  Half1 h1_even, h1_odd;
+  Scales sc_even, sc_odd;
   half8_t a_cur[TM], b_cur[TN], a_nxt[TM], b_nxt[TN];
 
-  auto read_half0 = [&](int buf) __attribute__((always_inline)) {
+  // This lane's fragment reads inside a ring slot.  Rows wm + 32 i + fr
+  // share the swizzle of row fr (wm and 32 i are multiples of 16), so
+  // fragment i lies a compile-time 32 i rows past fragment 0 and one base
+  // address per array and stage serves every fragment.
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "fragment rows share the swizzle of fr");
+  const int fr_sw = swz(fr);
+  const uint32_t off_a0 = kCodesA + (wm + fr) * kCodeRow + (((2 * fh) ^ fr_sw) << 4);
+  const uint32_t off_a1 = kCodesA + (wm + fr) * kCodeRow + (((2 * fh + 1) ^ fr_sw) << 4);
+  const uint32_t off_b0 = kCodesB + (wn + fr) * kCodeRow + (((2 * fh) ^ fr_sw) << 4);
+  const uint32_t off_b1 = kCodesB + (wn + fr) * kCodeRow + (((2 * fh + 1) ^ fr_sw) << 4);
+  const uint32_t off_as = kScalesA + (wm + fr) * kScaleRow + fh * 4;
+  const uint32_t off_bs = kScalesB + (wn + fr) * kScaleRow + fh * 4;
+
+  auto read_half0 = [&](int buf, Scales& sn) __attribute__((always_inline)) {
     const uint8_t* base = lds + buf * kStageBytes;
+    const uint8_t* pa = base + off_a0;
+    const uint8_t* pas = base + off_as;
+    const uint8_t* pb = base + off_b0;
+    const uint8_t* pbs = base + off_bs;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int row = wm + i * 32 + fr;
-      ac0[i] = *reinterpret_cast<const u32x4*>(base + kCodesA + chunk_off(row, 2 * fh));
-      asn[i] = *reinterpret_cast<const uint32_t*>(base + kScalesA + row * kScaleRow + fh * 4);
+      ac0[i] = *reinterpret_cast<const u32x4*>(pa + i * 32 * kCodeRow);
+      sn.a[i] = *reinterpret_cast<const uint32_t*>(pas + i * 32 * kScaleRow);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int row = wn + j * 32 + fr;
-      bc0[j] = *reinterpret_cast<const u32x4*>(base + kCodesB + chunk_off(row, 2 * fh));
-      bsn[j] = *reinterpret_cast<const uint32_t*>(base + kScalesB + row * kScaleRow + fh * 4);
+      bc0[j] = *reinterpret_cast<const u32x4*>(pb + j * 32 * kCodeRow);
+      sn.b[j] = *reinterpret_cast<const uint32_t*>(pbs + j * 32 * kScaleRow);
     }
   };
-  auto take_scales = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) asc[i] = asn[i];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bsc[j] = bsn[j];
-  };
-  auto read_half1 = [&](int buf) __attribute__((always_inline)) {
+  auto read_half1 = [&](int buf, Half1& h) __attribute__((always_inline)) {
     const uint8_t* base = lds + buf * kStageBytes;
+    const uint8_t* pa = base + off_a1;
+    const uint8_t* pb = base + off_b1;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      ac1[i] = *reinterpret_cast<const u32x4*>(base + kCodesA + chunk_off(wm + i * 32 + fr, 2 * fh + 1));
+    for (int i = 0; i < TM; ++i) h.a[i] = *reinterpret_cast<const u32x4*>(pa + i * 32 * kCodeRow);
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      bc1[j] = *reinterpret_cast<const u32x4*>(base + kCodesB + chunk_off(wn + j * 32 + fr, 2 * fh + 1));
+    for (int j = 0; j < TN; ++j) h.b[j] = *reinterpret_cast<const u32x4*>(pb + j * 32 * kCodeRow);
   };
   auto word = [](const u32x4 c, int s) __attribute__((always_inline)) {
     return (s & 3) == 0 ? c.x : (s & 3) == 1 ? c.y : (s & 3) == 2 ? c.z : c.w;
   };
-  auto decode_with = [&](int s, half8_t (&ad)[TM], half8_t (&bd)[TN], const uint32_t (&sa)[TM],
-                         const uint32_t (&sb)[TN]) __attribute__((always_inline)) {
+  // decoded operands of step s of a stage whose second half and scales are
+  // h1 and sc (its first half is in ac0/bc0)
+  auto decode_step = [&](int s, half8_t (&ad)[TM], half8_t (&bd)[TN], const Half1& h1,
+                         const Scales& sc) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      ad[i] = decode8(word(s < 4 ? ac0[i] : ac1[i], s),
-                      scale_pair_bits((sa[i] >> (8 * (s >> 1))) & 0xFF));
+      ad[i] = decode8(word(s < 4 ? ac0[i] : h1.a[i], s),
+                      scale_pair_bits((sc.a[i] >> (8 * (s >> 1))) & 0xFF));
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      bd[j] = decode8(word(s < 4 ? bc0[j] : bc1[j], s),
-                      scale_pair_bits((sb[j] >> (8 * (s >> 1))) & 0xFF));
-  };
-  auto decode_step = [&](int s, half8_t (&ad)[TM], half8_t (&bd)[TN]) __attribute__((always_inline)) {
-    decode_with(s, ad, bd, asc, bsc);
+      bd[j] = decode8(word(s < 4 ? bc0[j] : h1.b[j], s),
+                      scale_pair_bits((sc.b[j] >> (8 * (s >> 1))) & 0xFF));
   };
   auto mfma_step = [&](const half8_t (&ad)[TM], const half8_t (&bd)[TN]) __attribute__((always_inline)) {
 #pragma unroll
@@ -493,10 +508,9 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
     __syncthreads();
   }
   for (;;) {                                   // tiles (one unless kPersist)
-  read_half0(slot(0));
-  read_half1(slot(0));
-  take_scales();
-  decode_step(0, a_cur, b_cur);
+  read_half0(slot(0), sc_even);
+  read_half1(slot(0), h1_even);
+  decode_step(0, a_cur, b_cur, h1_even, sc_even);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -504,7 +518,10 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  for (int kt = 0; kt < nk; ++kt) {
+  // Stage kt, whose second half and scales are in h1/sc; the next stage's
+  // go to h1n/sn.
+  auto k_stage = [&](int kt, const Half1& h1, const Scales& sc, Half1& h1n, Scales& sn)
+      __attribute__((always_inline)) {
     if constexpr (kPersist) {
       // from here on the DMA loads the next tile's stages 0, 1, 2 (the slots
       // after this tile's last stage), if there is a next tile
@@ -522,11 +539,11 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
     // the next tile's stage 0 (kPersist) or is unused
     const int nbuf = slot(kt + 1);
     int nd = dma_group(kt, 0);
-    decode_step(1, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave(nd);
+    decode_step(1, a_nxt, b_nxt, h1, sc);  mfma_step(a_cur, b_cur);  interleave(nd);
     nd = dma_group(kt, 1);
-    decode_step(2, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);  interleave(nd);
+    decode_step(2, a_cur, b_cur, h1, sc);  mfma_step(a_nxt, b_nxt);  interleave(nd);
     nd = dma_group(kt, 2);
-    decode_step(3, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave(nd);
+    decode_step(3, a_nxt, b_nxt, h1, sc);  mfma_step(a_cur, b_cur);  interleave(nd);
     // Stage kt + 1 must have landed (every wave's loads) before its
     // fragments are read; the loads of stages kt + 2 .. kt + kRing - 1 stay in
     // flight.  The barrier also ends every wave's reads of stage kt (all
@@ -544,26 +561,42 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
       }
       __builtin_amdgcn_s_barrier();
     }
-    read_half0(nbuf);                       // next stage: words of steps 0-3, scales
+    // the next stage: its first half and scales during step 4, its second
+    // half (other registers than this stage's) during step 5
+    read_half0(nbuf, sn);
     nd = dma_group(kt, 3);
-    decode_step(4, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);
+    decode_step(4, a_cur, b_cur, h1, sc);  mfma_step(a_nxt, b_nxt);
     interleave(nd, 0, kHalf0Reads);
+    read_half1(nbuf, h1n);
     nd = dma_group(kt, 4);
-    decode_step(5, a_nxt, b_nxt);  mfma_step(a_cur, b_cur);  interleave(nd);
+    decode_step(5, a_nxt, b_nxt, h1, sc);  mfma_step(a_cur, b_cur);
+    interleave(nd, kDmaPer, kDmaPer + kHalf1Reads);
     nd = dma_group(kt, 5);
-    decode_step(6, a_cur, b_cur);  mfma_step(a_nxt, b_nxt);  interleave(nd);
-    // step 6 also reads the next stage's second half once step 7's words are
-    // decoded (consumed at the next stage's step 3)
-    decode_step(7, a_nxt, b_nxt);
-    mfma_step(a_cur, b_cur);
-    read_half1(nbuf);
-    interleave(0, TM * TN - kHalf1Reads, TM * TN);
-    // step 7: decode the next stage's step 0 (its first half and scales are
-    // in registers since step 3) under this stage's last MFMAs
-    decode_with(0, a_cur, b_cur, asn, bsn);
+    decode_step(6, a_cur, b_cur, h1, sc);  mfma_step(a_nxt, b_nxt);  interleave(nd);
+    decode_step(7, a_nxt, b_nxt, h1, sc);  mfma_step(a_cur, b_cur);  interleave();
+    // step 7: decode the next stage's step 0 under this stage's last MFMAs
+    decode_step(0, a_cur, b_cur, h1n, sn);
     mfma_step(a_nxt, b_nxt);
     interleave();
-    take_scales();
+    // the next stage's step-0 operands are complete here (keeps their decode
+    // under this stage's MFMAs rather than at the top of the next stage)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) asm volatile("" ::"v"(a_cur[i]));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) asm volatile("" ::"v"(b_cur[j]));
+  };
+  // two stages an iteration, so that the register sets alternate statically
+  // (an exit between the two would make the accumulators' registers differ
+  // at the two exits); an odd last stage follows the loop.  The tile walk is
+  // launched for an even number of stages only, which keeps that extra copy
+  // of the stage (and the registers it needs) out of it.
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    k_stage(kt, h1_even, sc_even, h1_odd, sc_odd);
+    k_stage(kt + 1, h1_odd, sc_odd, h1_even, sc_even);
+  }
+  if constexpr (!kPersist) {
+    if (kt < nk) k_stage(kt, h1_even, sc_even, h1_odd, sc_odd);
   }
 
   // ---- epilogue ------------------------------------------------------------
@@ -823,13 +856,13 @@ hipError_t launch_tiles(const W4A4Args& a, hipStream_t stream) {
   if (a.group_offsets != nullptr) tiles_m += a.num_groups;
   const int tiles_n = (int)((a.N + BN - 1) / BN);
   // persistent walk: the DMA path with a 4-deep ring, dense, one output type
-  // (its bands fit one ring slot), at least 4 stages and two tiles per CU;
-  // the NVFP4_PATH_GEMM_GRID flag turns it off
+  // (its bands fit one ring slot), an even number of at least 4 stages and
+  // two tiles per CU; the NVFP4_PATH_GEMM_GRID flag turns it off
   if constexpr (kRing == 4 && !kFused) {
     const bool allowed = (path_flags() & kPathGemmGrid) == 0;
     const int64_t n_tiles = (int64_t)tiles_m * tiles_n;
     const int cus = cu_count();
-    if (allowed && a.K % kBK == 0 && a.K / kBK >= 4 && a.group_offsets == nullptr &&
+    if (allowed && a.K % (2 * kBK) == 0 && a.K / kBK >= 4 && a.group_offsets == nullptr &&
         a.a_row_index == nullptr && (kSilu || ((a.y_f32 != nullptr) != (a.y_bf16 != nullptr))) &&
         n_tiles >= 2 * (int64_t)cus) {
       hipLaunchKernelGGL((w4a4_gemm_kernel<BM, BN, true, false, kRing, kOcc, kSilu, true>),
