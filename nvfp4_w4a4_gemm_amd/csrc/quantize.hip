@@ -260,64 +260,17 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(
   }
 }
 
-// Per E4M3 scale byte sb, where its blocks find their codes in the code
-// table: the row of its mantissa class starts at lo = 1024 k and an
-// element's index is its magnitude bits plus code_off + delta, delta = lo -
-// 128 e (sigma = (1 + k/8) 2^e).  Both as 16-bit pairs, for packed
-// arithmetic on two elements at once.  Byte 0 (sigma = 0) sends every index
-// below the table, i.e. to code 0.
-struct RowDesc {
-  uint32_t lo2;      // lo in both halves
-  uint32_t delta2;   // delta in both halves (int16)
-};
-
-__device__ __forceinline__ RowDesc row_desc(uint32_t sb) {
-  RowDesc d;
-  if (sb == 0) {
-    d.lo2 = 0;
-    d.delta2 = 0x80008000u;                 // -32768: saturates below lo
-  } else {
-    int e, k;
-    scale_class(sb, e, k);
-    const int lo = k * kCodeLutRow;
-    const int delta = lo - 128 * e;
-    d.lo2 = (uint32_t)lo * 0x10001u;
-    d.delta2 = ((uint32_t)delta & 0xFFFFu) * 0x10001u;
-  }
-  return d;
-}
-
-// Signs of the 8 BF16 values of w[4] at bit 3 of their code nibbles.
-__device__ __forceinline__ uint32_t sign_nibbles(const uint32_t (&w)[4]) {
-  // bytes 1 and 3 of each word hold the signs (bit 7) of its two values
-  const uint32_t a = __builtin_amdgcn_perm(w[1], w[0], 0x07050301u);   // e0 e1 e2 e3
-  const uint32_t b = __builtin_amdgcn_perm(w[3], w[2], 0x07050301u);   // e4 e5 e6 e7
-  const uint32_t even = __builtin_amdgcn_perm(b, a, 0x06040200u);      // e0 e2 e4 e6
-  const uint32_t odd = __builtin_amdgcn_perm(b, a, 0x07050301u);       // e1 e3 e5 e7
-  return ((even >> 4) & 0x08080808u) | (odd & 0x80808080u);
-}
-
-typedef short i16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
-
 // Dense tensor, flat segments as in amax_flat_kernel.  A 16-byte chunk is
 // half a block: lanes 2c and 2c + 1 hold the two halves of one block and
 // exchange their maxima (DPP quad permutation [1,0,3,2]).  Each lane writes
 // the 4 code bytes of its chunk (chunk c -> codes word c), the even lane the
 // scale byte (block c / 2).  n is even, so a block's two chunks are both in
-// range or both out.
-//
-// The tables' loads are issued before the first segment's: loads return in
-// order, so the tables can be copied to LDS while the data is in flight.
-// Magnitudes, indices and clamps are formed two values at a time in 16-bit
-// halves.
+// range or both out.  The tables' loads go before the first segment's (see
+// copy_tables_first).
 __global__ __launch_bounds__(kThreads) void quantize_flat_kernel(
     const u32x4* __restrict__ x, uint64_t n, const uint8_t* __restrict__ ws,
     uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  __shared__ __align__(16) uint8_t lds_sig[kSigLutN];
-  __shared__ __align__(16) uint8_t lds_code[kCodeLutN];
-  __shared__ RowDesc lds_desc[128];
-  static_assert(kSigLutN / 16 <= kThreads && kCodeLutN / 16 == 2 * kThreads, "table copy shape");
+  __shared__ TableLds tl;
   const int tid = threadIdx.x, lane = tid & 63;
   const uint64_t nwaves = (uint64_t)gridDim.x * (kThreads / 64);
   auto load_seg = [&](uint64_t seg, u32x4 (&v)[4]) __attribute__((always_inline)) {
@@ -328,23 +281,13 @@ __global__ __launch_bounds__(kThreads) void quantize_flat_kernel(
   };
   uint64_t seg = (uint64_t)blockIdx.x * (kThreads / 64) + (tid >> 6);
   u32x4 v[4];
-  {
-    const u32x4* sig = reinterpret_cast<const u32x4*>(ws + kWsSigLut);
-    const u32x4* code = reinterpret_cast<const u32x4*>(ws + kWsCodeLut);
-    const u32x4 t0 = tid < kSigLutN / 16 ? sig[tid] : u32x4{0u, 0u, 0u, 0u};
-    const u32x4 t1 = code[tid], t2 = code[tid + kThreads];
-    load_seg(seg, v);
-    if (tid < kSigLutN / 16) reinterpret_cast<u32x4*>(lds_sig)[tid] = t0;
-    reinterpret_cast<u32x4*>(lds_code)[tid] = t1;
-    reinterpret_cast<u32x4*>(lds_code)[tid + kThreads] = t2;
-    if (tid < 128) lds_desc[tid] = row_desc(tid);
-  }
+  copy_tables_first(ws, tl, tid, [&] { load_seg(seg, v); });
   const QuantParams P = *reinterpret_cast<const QuantParams*>(ws + kWsParams);
   __syncthreads();
 
   if (P.slow) {
     // alpha's exponent beyond +-100: the generic block path rescales first
-    const BlockTables t = tables_from(ws, lds_sig, lds_code);
+    const BlockTables t = tables_from(ws, tl.sig, tl.code);
     for (; seg * kSegChunks < n; seg += nwaves) {
       const uint64_t c0 = seg * kSegChunks + lane;
 #pragma unroll
@@ -370,40 +313,14 @@ __global__ __launch_bounds__(kThreads) void quantize_flat_kernel(
     return;
   }
 
-  const uint32_t code_off2 = ((uint32_t)P.code_off & 0xFFFFu) * 0x10001u;
-  const int sig_off = P.sig_off;
+  const FastTables t = fast_tables(tl, P);
   while (seg * kSegChunks < n) {
     const uint64_t c0 = seg * kSegChunks + lane;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      uint32_t mw[4];                        // magnitudes, two a word
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mw[i] = w[i] & 0x7FFF7FFFu;
-      const u16x2v mx = __builtin_elementwise_max(
-          __builtin_elementwise_max(__builtin_bit_cast(u16x2v, mw[0]), __builtin_bit_cast(u16x2v, mw[1])),
-          __builtin_elementwise_max(__builtin_bit_cast(u16x2v, mw[2]), __builtin_bit_cast(u16x2v, mw[3])));
-      uint32_t amax = max((uint32_t)mx.x, (uint32_t)mx.y);
-      amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0xB1, 0xF, 0xF, false));
-      const int sidx = min(max((int)amax + sig_off, 0), kSigLutN - 1);
-      const uint32_t sb = lds_sig[sidx];
-      const RowDesc d = lds_desc[sb];
-      // index = clamp(magnitude + off, lo, lo + 1023), two values at a time
-      // (the sum saturates; off and lo fit 16 bits for |shift| <= 100)
-      const i16x2 off2 = __builtin_elementwise_add_sat(__builtin_bit_cast(i16x2, code_off2),
-                                                       __builtin_bit_cast(i16x2, d.delta2));
-      const i16x2 lo2 = __builtin_bit_cast(i16x2, d.lo2);
-      const i16x2 hi2 = lo2 + (i16x2){(short)(kCodeLutRow - 1), (short)(kCodeLutRow - 1)};
-      uint32_t o = sign_nibbles(w);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        i16x2 idx = __builtin_elementwise_add_sat(__builtin_bit_cast(i16x2, mw[i]), off2);
-        idx = __builtin_elementwise_min(__builtin_elementwise_max(idx, lo2), hi2);
-        const uint32_t p = __builtin_bit_cast(uint32_t, idx);
-        const uint32_t c_lo = lds_code[p & 0xFFFFu];
-        const uint32_t c_hi = lds_code[p >> 16];
-        o |= (c_lo << (8 * i)) | (c_hi << (8 * i + 4));
-      }
+      uint32_t sb;
+      const uint32_t o = quantize_half_block(w, t, sb);
       const uint64_t c = c0 + 64 * u;
       if (c < n) {
         codes[c] = o;

@@ -20,7 +20,7 @@
 // RMSNorm) + 2 + 2.5625 (the quantiser) unfused.
 //
 // r and y are computed by one device function in both passes: fixed-order
-// fused multiply-add sums of the squares per lane, a butterfly over the wave
+// two-term dot products summing the squares per lane, a butterfly over the wave
 // (every lane ends with the same sum, as float addition is commutative),
 // IEEE division and square root, and y = (x * r) * gamma, so pass 3
 // reproduces pass 1's y bit for bit.
@@ -55,6 +55,14 @@ __device__ __forceinline__ void load_row(const uint16_t* __restrict__ xr, int nc
   }
 }
 
+// acc + lo^2 + hi^2 of the two BF16 values packed in w, in one two-term
+// dot product (the same instruction in both passes, so the same bits)
+__device__ __forceinline__ float sq2(uint32_t w, float acc) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const bf16x2v b = __builtin_bit_cast(bf16x2v, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(b, b, acc, false);
+}
+
 // r = 1 / sqrt(mean(x^2) + eps); the same value on every lane.
 template <int CH>
 __device__ __forceinline__ float row_inv_rms(const Row<CH>& row, int K, float eps) {
@@ -64,11 +72,7 @@ __device__ __forceinline__ float row_inv_rms(const Row<CH>& row, int K, float ep
   for (int j = 0; j < CH; ++j) {
     const uint32_t w[4] = {row.x[j].x, row.x[j].y, row.x[j].z, row.x[j].w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xFFFF0000u);
-      part[i] = __builtin_fmaf(lo, lo, part[i]);
-      part[i] = __builtin_fmaf(hi, hi, part[i]);
-    }
+    for (int i = 0; i < 4; ++i) part[i] = sq2(w[i], part[i]);
   }
   float ss = (part[0] + part[1]) + (part[2] + part[3]);
 #pragma unroll
@@ -100,17 +104,18 @@ __device__ __forceinline__ u32x4 chunk_y(const u32x4 x, const u32x4 g, float r) 
 // lane always touches the same chunks, so gamma is loaded once; with kPre
 // the next row's x is loaded before the current row is processed, so one
 // row's HBM round trip overlaps the other's arithmetic.
-// `first` runs once, after the first row's loads are issued (the quantise
-// pass copies its tables there); every wave of the workgroup runs it, also a
-// wave without a row.
+// `first(load)` runs once and must call load() (which issues the first
+// row's loads); the quantise pass issues its table loads before it.  Every
+// wave of the workgroup runs it, also a wave without a row.
 template <int CH, bool kPre, typename First, typename Body>
 __device__ __forceinline__ void for_rows(const uint16_t* __restrict__ x, int M, int nc,
                                          int64_t ld_x, int lane, First first, Body body) {
   const int stride = gridDim.x * kRowsPerBlock;
   int rowi = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   Row<CH> cur;
-  if (rowi < M) load_row<CH>(x + rowi * ld_x, nc, lane, cur);
-  first();
+  first([&] {
+    if (rowi < M) load_row<CH>(x + rowi * ld_x, nc, lane, cur);
+  });
   if (rowi >= M) return;
   while (true) {
     const int nxt = rowi + stride;
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_amax_kernel(
   u32x4 g[CH];
   load_gamma<CH>(gamma, nc, lane, g);
   uint32_t m = 0;
-  for_rows<CH, kPre>(x, M, nc, ld_x, lane, [] {}, [&](int, const Row<CH>& row) {
+  for_rows<CH, kPre>(x, M, nc, ld_x, lane, [](auto load) { load(); }, [&](int, const Row<CH>& row) {
     const float r = row_inv_rms<CH>(row, K, eps);
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
@@ -167,54 +172,6 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_amax_kernel(
   }
 }
 
-template <int CH, bool kPre>
-__global__ __launch_bounds__(kThreads) void rmsnorm_quantize_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, int M, int K,
-    int64_t ld_x, float eps, const uint8_t* __restrict__ ws, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, uint16_t* __restrict__ y_out, int64_t ld_y) {
-  __shared__ __align__(16) uint8_t lds_sig[kSigLutN];
-  __shared__ __align__(16) uint8_t lds_code[kCodeLutN];
-  const int lane = threadIdx.x & 63;
-  const int nc = K / 8;
-  u32x4 g[CH];
-  load_gamma<CH>(gamma, nc, lane, g);
-  const BlockTables t = tables_from(ws, lds_sig, lds_code);
-  // the tables are copied while the first row's loads are in flight
-  auto tables = [&] {
-    load_tables_to_lds(ws, lds_sig, lds_code, threadIdx.x, kThreads);
-    __syncthreads();
-  };
-  for_rows<CH, kPre>(x, M, nc, ld_x, lane, tables, [&](int rowi, const Row<CH>& row) {
-    const float r = row_inv_rms<CH>(row, K, eps);
-    uint32_t* crow = reinterpret_cast<uint32_t*>(codes + (int64_t)rowi * (K / 2));
-    uint8_t* srow = scales + (int64_t)rowi * (K / 16);
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int c = lane + 64 * j;
-      // lanes 2i and 2i + 1 hold the two halves of a block (64 is even);
-      // every lane of the wave takes part in the exchange (past the row's
-      // end the values are zero and nothing is stored)
-      const u32x4 y = chunk_y(row.x[j], g[j], r);
-      const uint32_t w[4] = {y.x, y.y, y.z, y.w};
-      uint32_t mag[8];
-      magnitudes<4>(w, t, mag);
-      uint32_t amax = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = max(amax, mag[i]);
-      amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0xB1, 0xF, 0xF, false));
-      CodeRow cr;
-      const uint32_t sb = block_scale(amax, t, cr);
-      const uint32_t o = codes8(mag, w, cr, t);
-      if (c < nc) {
-        crow[c] = o;
-        if ((lane & 1) == 0) srow[c >> 1] = (uint8_t)sb;
-        if (y_out != nullptr) reinterpret_cast<u32x4*>(y_out + rowi * ld_y)[c] = y;
-      }
-      __builtin_amdgcn_sched_barrier(0);               // one chunk at a time (registers)
-    }
-  });
-}
-
 // ---- streaming variant (rows longer than 5120) -----------------------------
 // The row is not held in registers: it is read once for the sum of squares
 // and chunk by chunk again for y (the second read finds it in L2), gamma is
@@ -231,11 +188,7 @@ __device__ __forceinline__ float stream_inv_rms(const u32x4* __restrict__ xr, in
     const u32x4 v = c < nc ? xr[c] : u32x4{0u, 0u, 0u, 0u};
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xFFFF0000u);
-      part[i] = __builtin_fmaf(lo, lo, part[i]);
-      part[i] = __builtin_fmaf(hi, hi, part[i]);
-    }
+    for (int i = 0; i < 4; ++i) part[i] = sq2(w[i], part[i]);
   }
   float ss = (part[0] + part[1]) + (part[2] + part[3]);
 #pragma unroll
@@ -279,19 +232,17 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_amax_stream_kernel(
   }
 }
 
+// Rows of the wave, streamed: codes, scales (and y) of each.  slow: alpha's
+// exponent beyond +-100, the generic block path (which rescales first).
 template <int CH>
-__global__ __launch_bounds__(kThreads) void rmsnorm_quantize_stream_kernel(
+__device__ __forceinline__ void stream_rows_quantize(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, int M, int K,
-    int64_t ld_x, float eps, const uint8_t* __restrict__ ws, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, uint16_t* __restrict__ y_out, int64_t ld_y) {
-  __shared__ __align__(16) uint8_t lds_sig[kSigLutN];
-  __shared__ __align__(16) uint8_t lds_code[kCodeLutN];
+    int64_t ld_x, float eps, const BlockTables& tg, const FastTables& tf, bool slow,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint16_t* __restrict__ y_out,
+    int64_t ld_y) {
   const int lane = threadIdx.x & 63;
   const int nc = K / 8;
   const u32x4* g4 = reinterpret_cast<const u32x4*>(gamma);
-  load_tables_to_lds(ws, lds_sig, lds_code, threadIdx.x, kThreads);
-  const BlockTables t = tables_from(ws, lds_sig, lds_code);
-  __syncthreads();
   for (int rowi = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6); rowi < M;
        rowi += gridDim.x * kRowsPerBlock) {
     const u32x4* xr = reinterpret_cast<const u32x4*>(x + rowi * ld_x);
@@ -304,15 +255,20 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quantize_stream_kernel(
       const bool ok = c < nc;
       const u32x4 y = ok ? chunk_y(xr[c], g4[c], r) : u32x4{0u, 0u, 0u, 0u};
       const uint32_t w[4] = {y.x, y.y, y.z, y.w};
-      uint32_t mag[8];
-      magnitudes<4>(w, t, mag);
-      uint32_t amax = 0;
+      uint32_t o, sb;
+      if (slow) {
+        uint32_t mag[8];
+        magnitudes<4>(w, tg, mag);
+        uint32_t amax = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) amax = max(amax, mag[i]);
-      amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0xB1, 0xF, 0xF, false));
-      CodeRow cr;
-      const uint32_t sb = block_scale(amax, t, cr);
-      const uint32_t o = codes8(mag, w, cr, t);
+        for (int i = 0; i < 8; ++i) amax = max(amax, mag[i]);
+        amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0xB1, 0xF, 0xF, false));
+        CodeRow cr;
+        sb = block_scale(amax, tg, cr);
+        o = codes8(mag, w, cr, tg);
+      } else {
+        o = quantize_half_block(w, tf, sb);
+      }
       if (ok) {
         crow[c] = o;
         if ((lane & 1) == 0) srow[c >> 1] = (uint8_t)sb;
@@ -320,6 +276,68 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quantize_stream_kernel(
       }
     }
   }
+}
+
+template <int CH>
+__global__ __launch_bounds__(kThreads) void rmsnorm_quantize_stream_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, int M, int K,
+    int64_t ld_x, float eps, const uint8_t* __restrict__ ws, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, uint16_t* __restrict__ y_out, int64_t ld_y) {
+  __shared__ TableLds tl;
+  copy_tables_first(ws, tl, threadIdx.x, [] {});
+  const QuantParams P = *reinterpret_cast<const QuantParams*>(ws + kWsParams);
+  __syncthreads();
+  stream_rows_quantize<CH>(x, gamma, M, K, ld_x, eps, tables_from(ws, tl.sig, tl.code),
+                           fast_tables(tl, P), P.slow != 0, codes, scales, y_out, ld_y);
+}
+
+template <int CH, bool kPre>
+__global__ __launch_bounds__(kThreads) void rmsnorm_quantize_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, int M, int K,
+    int64_t ld_x, float eps, const uint8_t* __restrict__ ws, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, uint16_t* __restrict__ y_out, int64_t ld_y) {
+  __shared__ TableLds tl;
+  const int lane = threadIdx.x & 63;
+  const int nc = K / 8;
+  const QuantParams P = *reinterpret_cast<const QuantParams*>(ws + kWsParams);
+  if (P.slow) {
+    // alpha's exponent beyond +-100: the rows are streamed (as the streaming
+    // variant does, with the same r and y bits) through the generic block
+    // path, so that this rare path adds no registers to the held-row one
+    copy_tables_first(ws, tl, threadIdx.x, [] {});
+    __syncthreads();
+    stream_rows_quantize<CH>(x, gamma, M, K, ld_x, eps, tables_from(ws, tl.sig, tl.code),
+                             fast_tables(tl, P), true, codes, scales, y_out, ld_y);
+    return;
+  }
+  u32x4 g[CH];
+  load_gamma<CH>(gamma, nc, lane, g);
+  // the tables' loads go first, then the first row's (see copy_tables_first)
+  auto tables = [&](auto load) {
+    copy_tables_first(ws, tl, threadIdx.x, load);
+    __syncthreads();
+  };
+  for_rows<CH, kPre>(x, M, nc, ld_x, lane, tables, [&](int rowi, const Row<CH>& row) {
+    const FastTables t = fast_tables(tl, P);
+    const float r = row_inv_rms<CH>(row, K, eps);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      // lanes 2i and 2i + 1 hold the two halves of a block (64 is even);
+      // every lane of the wave takes part in the exchange (past the row's
+      // end the values are zero and nothing is stored)
+      const u32x4 y = chunk_y(row.x[j], g[j], r);
+      const uint32_t w[4] = {y.x, y.y, y.z, y.w};
+      uint32_t sb;
+      const uint32_t o = quantize_half_block(w, t, sb);
+      const int c = lane + 64 * j;
+      if (c < nc) {
+        reinterpret_cast<uint32_t*>(codes + (int64_t)rowi * (K / 2))[c] = o;
+        if ((lane & 1) == 0) (scales + (int64_t)rowi * (K / 16))[c >> 1] = (uint8_t)sb;
+        if (y_out != nullptr) reinterpret_cast<u32x4*>(y_out + rowi * ld_y)[c] = y;
+      }
+      __builtin_amdgcn_sched_barrier(0);               // one chunk at a time (registers)
+    }
+  });
 }
 
 template <int CH>

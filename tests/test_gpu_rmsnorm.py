@@ -76,6 +76,15 @@ def test_rmsnorm_quantize_zero_rows_tiny_eps_and_given_alpha():
     check(xb, gamma_bits(k, 6), 1e-5, alpha_in=2.0 ** -9)
 
 
+@pytest.mark.parametrize("m,k", [(37, 2816), (9, 6144), (5, 16), (64, 5120)])
+@pytest.mark.parametrize("alpha_in", [2.0 ** -120, 2.0 ** 110])
+def test_rmsnorm_quantize_extreme_given_alpha(m, k, alpha_in):
+    """alpha's exponent beyond +-100 (the rescaling block path) for rows held
+    in registers (K <= 5120) and streamed (K = 6144)."""
+    xb = normal_bits(m, k, seed=m + k)
+    check(xb, gamma_bits(k, 3), 1e-6, alpha_in=alpha_in)
+
+
 def test_rmsnorm_quantize_full_size():
     """The layer's X_qkv (8192 x 4096, outlier channels) at full size: every
     normalised value within one BF16 ulp of the oracle, alpha and every code
