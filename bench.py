@@ -581,7 +581,8 @@ def graph_ms(torch, fn, n, reps, check=None):
 def decode_block(nv, torch, dev, workspace, steps, warmup):
     """Decode-shaped W4A4 GEMMs of the same layer: the attention projections
     (QKV 7168x5120, then O 5120x5120) and the MLP (gate+up 51200x5120, then
-    down 5120x25600) at 1 and 16 tokens,
+    down 5120x25600), and a Qwen3-8B-shaped gate+up weight 24576x4096, at 1
+    and 16 tokens,
     each pair of launches timed with HIP events around replays of a HIP
     graph of the launches over all weight copies (a decode step's kernels
     are a few microseconds each, less than the host's cost to launch them
@@ -595,7 +596,8 @@ def decode_block(nv, torch, dev, workspace, steps, warmup):
     beside it."""
     gen = torch.Generator(device=dev)
     gen.manual_seed(2024)
-    parts = {"attention": [(7168, 5120), (5120, 5120)], "mlp": [(51200, 5120), (5120, 25600)]}
+    parts = {"attention": [(7168, 5120), (5120, 5120)], "mlp": [(51200, 5120), (5120, 25600)],
+             "qwen3_8b_gate_up": [(24576, 4096)]}
     rows = []
     for part, shapes in parts.items():
         wbytes = sum(n * k * 9 // 16 for n, k in shapes)

@@ -10,7 +10,10 @@
 //             sum_{k in b} q^a_{m,k} q^b_{n,k}
 //
 // At this shape the work is a stream over the weight codes (0.5625 bytes a
-// weight): the kernel is bound by HBM, not by the matrix cores.  Layout:
+// weight): the kernel is bound by HBM, not by the matrix cores.  One token
+// row (with K % 32 == 0, K <= 8192) takes the matrix-vector kernel
+// w4a4_gemv_kernel (whole weight rows a wave, described there); otherwise
+// the layout is:
 //
 //  - A workgroup (4 waves) owns 16 output columns and all of K.  The K axis
 //    is cut into 32-element chunks (16 code bytes and 2 scale bytes a row);
@@ -543,6 +546,131 @@ __global__ __launch_bounds__(kThreads * kG) void w4a4_decode_lds_kernel(
   }
 }
 
+// ---- one token row: a streamed matrix-vector product (K % 32 == 0) -------
+// With one token row a 16 x 16 MFMA would use one of its 16 A rows, and
+// staging K-slices of 16 weight rows breaks each row into 256-byte pieces.
+// Here a wave takes whole weight rows, one at a time, its lanes across K:
+// lane l owns the 32-element chunks c = l + 64 j (j < CH), reads the row's
+// 16 code bytes and 2 scale bytes of each, and keeps the token's values of
+// those chunks in registers, decoded once (q sigma 2^-4, exact in float16).
+// A weight block (16 values) contributes sigma_w times an exact sum: the
+// codes (exact float16) against the token values by two-term dot products
+// accumulating in float32 (every product and partial sum is a multiple of
+// sigma_a 2^-6 of at most 12 bits, so the sum is exact), then one multiply
+// by sigma_w 2^-8 (the E4M3 byte as a float16, exact) into the lane's
+// float32 sum.  The 64 lane sums of a row are added in a fixed DPP order
+// (lane 63 ends with the total) and scaled by alpha_a alpha_b 2^12.  The
+// row DEPTH rounds ahead is loaded while a row is reduced.
+// The 8 FP4 codes of w as 4 float16 pairs, times 2^e (e = exponent of f).
+struct Half2x4 {
+  half2_t h[4];
+};
+__device__ __forceinline__ Half2x4 cvt8(uint32_t w, float f) {
+  Half2x4 r;
+  r.h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, f, 0);
+  r.h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, f, 1);
+  r.h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, f, 2);
+  r.h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, f, 3);
+  return r;
+}
+
+template <int CH, int DEPTH>
+__global__ __launch_bounds__(kThreads) void w4a4_gemv_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const float* __restrict__ alpha_a, const uint8_t* __restrict__ b_codes,
+    const uint8_t* __restrict__ b_scales, const float* __restrict__ alpha_b,
+    const float* __restrict__ alpha_b_rows, int N, int K, float* __restrict__ y_f32,
+    uint16_t* __restrict__ y_bf16) {
+  const int lane = threadIdx.x & 63;
+  const int nc = K / 32;                              // chunks a row
+  const uint32_t row_codes = (uint32_t)(K / 2), row_scales = (uint32_t)(K / 16);
+  const __amdgpu_buffer_rsrc_t rbc = buffer_of(b_codes, (uint32_t)N * row_codes);
+  const __amdgpu_buffer_rsrc_t rbs = buffer_of(b_scales, (uint32_t)N * row_scales);
+
+  // the token's values of this lane's chunks (zero past the row end)
+  half2_t av[CH][16];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int c = lane + 64 * j;
+    const bool ok = c < nc;
+    const u32x4 w = ok ? reinterpret_cast<const u32x4*>(a_codes)[c] : u32x4{0u, 0u, 0u, 0u};
+    const uint32_t sb = ok ? (uint32_t)reinterpret_cast<const uint16_t*>(a_scales)[c] : 0u;
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const half2_t s = scale_pair((sb >> (8 * (q >> 1))) & 0xFFu);
+      const Half2x4 v = cvt8(ww[q], 16.0f);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) av[j][4 * q + h] = v.h[h] * s;
+    }
+  }
+
+  struct RowData {
+    u32x4 codes[CH];
+    uint32_t scales[CH];
+  };
+  auto load_row = [&](int n, RowData& d) __attribute__((always_inline)) {
+    const uint32_t rn = (uint32_t)(n < N ? n : N - 1);          // clamped: loads always valid
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = lane + 64 * j;
+      const uint32_t cc = (uint32_t)(c < nc ? c : nc - 1);
+      d.codes[j] = __builtin_amdgcn_raw_buffer_load_b128(rbc, rn * row_codes + 16u * cc, 0, 2);
+      d.scales[j] = __builtin_amdgcn_raw_buffer_load_b16(rbs, rn * row_scales + 2u * cc, 0, 0);
+    }
+  };
+  const int wstride = (int)gridDim.x * kWaves;
+  const int n0 = (int)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  RowData ring[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) load_row(n0 + d * wstride, ring[d]);
+  const float scale_a = (*alpha_a) * 4096.0f;
+
+  for (int n = n0; n < N; n += DEPTH * wstride) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int nd = n + d * wstride;
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int c = lane + 64 * j;
+        const uint32_t ww[4] = {ring[d].codes[j].x, ring[d].codes[j].y, ring[d].codes[j].z,
+                                ring[d].codes[j].w};
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {                  // the chunk's two blocks
+          float p = 0.0f;
+#pragma unroll
+          for (int q = 2 * b; q < 2 * b + 2; ++q) {
+            const Half2x4 wq = cvt8(ww[q], 1.0f);
+#pragma unroll
+            for (int h = 0; h < 4; ++h) p = __builtin_amdgcn_fdot2(wq.h[h], av[j][4 * q + h], p, false);
+          }
+          // sigma_w 2^-8: the E4M3 byte's fields in a float16's (a zero
+          // byte past the row end)
+          const uint32_t sb = c < nc ? (ring[d].scales[j] >> (8 * b)) & 0xFFu : 0u;
+          const float sw = (float)__builtin_bit_cast(_Float16, (uint16_t)(sb << 7));
+          acc = __builtin_fmaf(p, sw, acc);
+        }
+      }
+      // refill the slot with the row DEPTH rounds ahead
+      load_row(nd + DEPTH * wstride, ring[d]);
+      // lane 63 ends with the sum of the 64 lanes (gfx9 DPP reduction)
+      acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0xB1, 0xF, 0xF, false));
+      acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x4E, 0xF, 0xF, false));
+      acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x141, 0xF, 0xF, false));
+      acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x140, 0xF, 0xF, false));
+      acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x142, 0xA, 0xF, false));
+      acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x143, 0xC, 0xF, false));
+      if (lane == 63 && nd < N) {
+        const float ab = alpha_b_rows != nullptr ? alpha_b_rows[nd] : *alpha_b;
+        const float v = acc * (scale_a * ab);
+        if (y_f32 != nullptr) y_f32[nd] = v;
+        if (y_bf16 != nullptr) y_bf16[nd] = (uint16_t)f32_to_bf16_bits(v);
+      }
+    }
+  }
+}
+
 int device_cus() {
   static std::atomic<int> cached[64];
   int dev = 0;
@@ -617,6 +745,22 @@ hipError_t launch_one_mtile(const DecodeArgs& p, int n_stages, hipStream_t strea
   return launch_lds<1, 6, false, 1>(p, 6 * kStage, stream);
 }
 
+template <int CH>
+hipError_t launch_gemv(const DecodeArgs& p, hipStream_t stream) {
+  // one row in flight a wave and four rows a wave (measured best at
+  // 24576 x 4096 and 51200 x 5120 against 2-8 rows in flight and 2-16 rows
+  // a wave: fewer registers, more waves), at most 8 workgroups a CU
+  constexpr int kDepth = 1;
+  const int64_t waves = (p.N + 3) / 4;
+  int64_t wgs = (waves + kWaves - 1) / kWaves;
+  const int64_t cap = (int64_t)device_cus() * 8;
+  if (wgs > cap) wgs = cap;
+  hipLaunchKernelGGL((w4a4_gemv_kernel<CH, kDepth>), dim3((unsigned)wgs), dim3(kThreads), 0, stream,
+                     p.a_codes, p.a_scales, p.alpha_a, p.b_codes, p.b_scales, p.alpha_b,
+                     p.alpha_b_rows, (int)p.N, (int)p.K, p.y_f32, p.y_bf16);
+  return hipGetLastError();
+}
+
 template <int MT>
 hipError_t launch_mt(const DecodeArgs& p, hipStream_t stream) {
   const dim3 grid((unsigned)((p.N + kCols - 1) / kCols));
@@ -645,6 +789,15 @@ hipError_t launch_mt(const DecodeArgs& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_w4a4_decode(const DecodeArgs& p, hipStream_t stream) {
+  // one token row, whole 32-element chunks, at most 4 chunks a lane:
+  // whole weight rows a wave (written to column n of row 0; ld_y unused)
+  if (p.M == 1 && p.K % 32 == 0 && p.K <= 64 * 32 * 4 && (path_flags() & kPathDecodeDirect) == 0) {
+    const int64_t ch = (p.K / 32 + 63) / 64;
+    if (ch <= 1) return launch_gemv<1>(p, stream);
+    if (ch <= 2) return launch_gemv<2>(p, stream);
+    if (ch <= 3) return launch_gemv<3>(p, stream);
+    return launch_gemv<4>(p, stream);
+  }
   if (p.M <= 16) return launch_mt<1>(p, stream);
   if (p.M <= 32) return launch_mt<2>(p, stream);
   return launch_mt<4>(p, stream);

@@ -260,7 +260,9 @@ def test_w4a4_gemm_deterministic():
                                    (1, 4096, 4096), (3, 129, 4112), (48, 96, 544),
                                    (12, 40, 4096), (2, 2100, 1024), (3, 1000, 2560),
                                    (1, 6000, 1536), (12, 5000, 4096), (16, 9000, 512),
-                                   (14, 8400, 3072), (1, 20000, 512)])
+                                   (14, 8400, 3072), (1, 20000, 512),
+                                   (8, 300, 4096), (8, 6144, 4096), (8, 24576, 4096),
+                                   (7, 300, 4608)])
 def test_w4a4_gemm_decode_matches_oracle(m, n, k):
     """Decode shape (M <= 64): one, two and four 16-row tiles, K with a
     half chunk at the end (K % 32 == 16), a single column, ragged N; the
@@ -276,6 +278,47 @@ def test_w4a4_gemm_decode_matches_oracle(m, n, k):
     y32, y16 = nv.w4a4_gemm_decode(qa, qw)
     y, bound, y16_ref = orc.w4a4_reference(orc.quantize(xb), orc.quantize(wb))
     assert_gemm_close(y32, y16, y, bound, y16_ref)
+
+
+@pytest.mark.parametrize("n,k", [(33, 96), (5, 4128), (7, 8192), (300, 6144), (2, 32),
+                                 (1000, 5120), (24576, 4096)])
+def test_w4a4_gemm_decode_one_token(n, k):
+    """One token row: the matrix-vector kernel (whole weight rows a wave, a
+    lane's chunks across K) for 1 to 4 chunks a lane, K with lanes past the
+    row's end (96, 4128), and the layer's 24576 x 4096 gate+up weight at
+    full size, in both output types and against the LDS-staged kernel."""
+    xb, wb = quantized_pair(1, n, k, seed=n + 7 * k)
+    qa = nv.nvfp4_quantize_act(dev_bf16(xb))
+    qw = nv.nvfp4_quantize_weights(dev_bf16(wb))
+    y, bound, y16_ref = orc.w4a4_reference(orc.quantize(xb), orc.quantize(wb))
+    y32, y16 = nv.w4a4_gemm_decode(qa, qw)
+    assert_gemm_close(y32, y16, y, bound, y16_ref)
+    o32 = torch.full((1, n + 5), 7.0, device=DEV)
+    o16 = torch.full((1, n + 5), 7.0, device=DEV, dtype=torch.bfloat16)
+    nv.w4a4_gemm_decode(qa, qw, y_f32=o32[:, :n], bf16=False)
+    nv.w4a4_gemm_decode(qa, qw, f32=False, y_bf16=o16[:, :n])
+    assert torch.equal(o32[:, :n], y32) and torch.equal(o16[:, :n].view(torch.int16), y16.view(torch.int16))
+    assert torch.all(o32[:, n:] == 7.0) and torch.all(o16[:, n:] == 7.0)
+
+
+def test_w4a4_gemm_decode_one_token_stacked_weights():
+    """One token row against weights stacked along N under three tensor
+    scales (per-row alpha), with subnormal block scales."""
+    k = 2048
+    rng = np.random.default_rng(79)
+    x = (rng.standard_normal((1, k)) * 0.01).astype(np.float32)
+    x[0, 5] = 1000.0
+    xb = bf16_bits(x)
+    ra = orc.quantize(xb)
+    parts = [bf16_bits((rng.standard_normal((n, k)) * std).astype(np.float32))
+             for n, std in ((64, 0.0002), (40, 0.5), (30, 3.0))]
+    qa = nv.nvfp4_quantize_act(dev_bf16(xb))
+    qws = [nv.nvfp4_quantize_weights(dev_bf16(w)) for w in parts]
+    stack = nv.stack_tensors(qws)
+    y32, y16 = nv.w4a4_gemm_decode(qa, stack)
+    for q, w, lo, hi in zip(qws, parts, stack.offsets[:-1], stack.offsets[1:]):
+        y, bound, y16_ref = orc.w4a4_reference(ra, orc.quantize(w))
+        assert_gemm_close(y32[:, lo:hi], y16[:, lo:hi], y, bound, y16_ref)
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (20, 64, 2816), (64, 33, 512)])
