@@ -281,12 +281,15 @@ def test_w4a4_gemm_decode_matches_oracle(m, n, k):
 
 
 @pytest.mark.parametrize("n,k", [(33, 96), (5, 4128), (7, 8192), (300, 6144), (2, 32),
-                                 (1000, 5120), (24576, 4096)])
+                                 (1000, 5120), (24576, 4096), (40, 8224), (300, 25600),
+                                 (3, 32768), (5120, 12288), (64, 20480)])
 def test_w4a4_gemm_decode_one_token(n, k):
     """One token row: the matrix-vector kernel (whole weight rows a wave, a
     lane's chunks across K) for 1 to 4 chunks a lane, K with lanes past the
-    row's end (96, 4128), and the layer's 24576 x 4096 gate+up weight at
-    full size, in both output types and against the LDS-staged kernel."""
+    row's end (96, 4128), the layer's 24576 x 4096 gate+up weight at full
+    size, and its long-row variant (token in LDS: K from 8224 to 32768,
+    rounds of 4 chunks a lane with lanes past the end), in both output
+    types and into a wider output."""
     xb, wb = quantized_pair(1, n, k, seed=n + 7 * k)
     qa = nv.nvfp4_quantize_act(dev_bf16(xb))
     qw = nv.nvfp4_quantize_weights(dev_bf16(wb))
