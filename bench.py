@@ -870,7 +870,9 @@ def counter_pass():
       3. the gate+up W4A4 GEMM 16384 x 51200 x 5120 (BF16 out), three times;
       4. the BF16 comparison GEMM and torch.matmul of the same shape, once each;
       5. the decode-shaped W4A4 GEMM of one token against a seeded
-         N(0, 0.02) 24576 x 4096 weight made on the device, three times.
+         N(0, 0.02) 24576 x 4096 weight made on the device, three times;
+      6. the quantiser and the fused RMSNorm + quantiser on a seeded N(0, 1)
+         8192 x 4096 activation, three times each.
     """
     import torch
     from nvfp4_w4a4_gemm_amd import binding as nv
@@ -918,6 +920,17 @@ def counter_pass():
     torch.cuda.synchronize()
     for _ in range(3):
         nv.w4a4_gemm_decode(qt, qgu, f32=False, y_bf16=yd)
+    torch.cuda.synchronize()
+    del qgu
+    print("quantize and rmsnorm+quantize 8192x4096 x3", flush=True)
+    xa = torch.randn(8192, 4096, device=dev, generator=gen).to(torch.bfloat16)
+    ga = (1.0 + 0.1 * torch.randn(4096, device=dev, generator=gen)).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        nv.nvfp4_quantize_act(xa, workspace=ws)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        nv.nvfp4_rmsnorm_quantize_act(xa, ga, 1e-6, workspace=ws)
     torch.cuda.synchronize()
     print("done", flush=True)
 
