@@ -872,7 +872,9 @@ def counter_pass():
       5. the decode-shaped W4A4 GEMM of one token against a seeded
          N(0, 0.02) 24576 x 4096 weight made on the device, three times;
       6. the quantiser and the fused RMSNorm + quantiser on a seeded N(0, 1)
-         8192 x 4096 activation, three times each.
+         8192 x 4096 activation, three times each;
+      7. the down W4A4 GEMM 16384 x 5120 x 25600 (BF16 out) three times, then
+         torch.matmul of that shape once.
     """
     import torch
     from nvfp4_w4a4_gemm_amd import binding as nv
@@ -931,6 +933,19 @@ def counter_pass():
     torch.cuda.synchronize()
     for _ in range(3):
         nv.nvfp4_rmsnorm_quantize_act(xa, ga, 1e-6, workspace=ws)
+    torch.cuda.synchronize()
+    del xa, ga
+    print("w4a4 gemm down 16384x5120x25600 x3", flush=True)
+    hd = nv.to_device_bf16(wl.tensors["H"].full(), dev)
+    wd = nv.to_device_bf16(wl.tensors["W_down"].full(), dev)
+    qh = nv.nvfp4_quantize_act(hd, workspace=ws)
+    qwd = nv.nvfp4_quantize_weights(wd, workspace=ws)
+    yd = torch.empty(hd.shape[0], wd.shape[0], dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        nv.w4a4_gemm(qh, qwd, f32=False, y_bf16=yd)
+    torch.cuda.synchronize()
+    torch.matmul(hd, wd.t())
     torch.cuda.synchronize()
     print("done", flush=True)
 
