@@ -212,13 +212,24 @@ nvfp4_status_t w4a4_gemm_multi(const uint8_t* a_codes, const uint8_t* a_scales,
  *   gamma_bf16  [K] BF16 weights (16-byte aligned)
  *   K           a multiple of 16, at most 8192 (the row is held in registers)
  *   eps         >= 0
- *   alpha_in, alpha_out, codes, scales, workspace: as nvfp4_quantize_act
+ *   alpha_in, alpha_out, codes, scales: as nvfp4_quantize_act
+ *   workspace   device scratch of at least nvfp4_workspace_bytes() bytes;
+ *               with nvfp4_rmsnorm_workspace_bytes(M) bytes or more (and
+ *               alpha_in null) the amax pass of rows longer than 5120 also
+ *               stores each row's r there and the quantise pass reads it
+ *               instead of reading the row twice (a faster kernel, the same
+ *               results)
  *   y_bf16      nullable: when set, y itself is also written, [M][ld_y]
  *               (16-byte aligned, ld_y a multiple of 8, ld_y >= K)
- * The two passes read x twice (the row's r is computed again, by the same
- * arithmetic, so both passes see the same y).  Errors and ownership as for
- * nvfp4_quantize_act.
+ * The two passes read x twice; both see the same y, whether r is summed in
+ * each pass by the same arithmetic or stored by the first.  Errors and
+ * ownership as for nvfp4_quantize_act.
  */
+/* Workspace bytes with which nvfp4_rmsnorm_quantize_act keeps each row's r
+ * between its passes (nvfp4_workspace_bytes() plus 4 bytes a row, rounded);
+ * 0 for M < 0. */
+size_t nvfp4_rmsnorm_workspace_bytes(int64_t M);
+
 nvfp4_status_t nvfp4_rmsnorm_quantize_act(const void* x_bf16, const void* gamma_bf16, int64_t M,
                                           int64_t K, int64_t ld_x, float eps,
                                           const float* alpha_in, float* alpha_out,

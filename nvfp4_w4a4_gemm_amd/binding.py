@@ -54,6 +54,7 @@ _SIGNATURES = {
 
 EXPORTS = sorted(list(_SIGNATURES) + ["nvfp4_status_string", "nvfp4_workspace_bytes",
                                       "w4a4_gemm_silu_mul_workspace_bytes",
+                                      "nvfp4_rmsnorm_workspace_bytes",
                                       "nvfp4_set_path_flags", "nvfp4_path_flags"])
 
 # kernel-path flags (nvfp4_set_path_flags), for tests and benchmarks
@@ -93,6 +94,8 @@ def lib() -> ctypes.CDLL:
         handle.nvfp4_workspace_bytes.restype = ctypes.c_size_t
         handle.w4a4_gemm_silu_mul_workspace_bytes.argtypes = [_c_i64, _c_i64]
         handle.w4a4_gemm_silu_mul_workspace_bytes.restype = ctypes.c_size_t
+        handle.nvfp4_rmsnorm_workspace_bytes.argtypes = [_c_i64]
+        handle.nvfp4_rmsnorm_workspace_bytes.restype = ctypes.c_size_t
         handle.nvfp4_set_path_flags.argtypes = [ctypes.c_int]
         handle.nvfp4_set_path_flags.restype = None
         handle.nvfp4_path_flags.argtypes = []
@@ -138,6 +141,13 @@ def workspace_bytes() -> int:
 
 def new_workspace(device) -> torch.Tensor:
     return torch.empty(workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+def rmsnorm_workspace(m: int, device) -> torch.Tensor:
+    """Workspace with which nvfp4_rmsnorm_quantize_act keeps each of m rows'
+    r between its two passes (the faster quantise pass)."""
+    return torch.empty(int(lib().nvfp4_rmsnorm_workspace_bytes(m)), dtype=torch.uint8,
+                       device=device)
 
 
 @dataclass
@@ -272,7 +282,9 @@ def nvfp4_rmsnorm_quantize_act(x: torch.Tensor, gamma: torch.Tensor, eps: float,
                                workspace: torch.Tensor | None = None) -> NVFP4Tensor:
     """RMSNorm of a BF16 activation [M, K] with weights gamma [K], produced
     directly as NVFP4 (alpha from the normalised tensor unless given); y_out
-    (BF16 [M, K] view) also receives the normalised values when given."""
+    (BF16 [M, K] view) also receives the normalised values when given.
+    Without a workspace one of rmsnorm_workspace(M) is made; a smaller one
+    (at least new_workspace's) selects the pass that sums each row again."""
     _check_bf16_2d(x, "x")
     m, k = x.shape
     if gamma.dtype != torch.bfloat16 or gamma.shape != (k,) or not gamma.is_contiguous():
@@ -293,7 +305,7 @@ def nvfp4_rmsnorm_quantize_act(x: torch.Tensor, gamma: torch.Tensor, eps: float,
     _check_alpha(out.alpha, 1, dev, "out.alpha")
     if alpha_in is not None:
         _check_alpha(alpha_in, 1, dev, "alpha_in")
-    ws = workspace if workspace is not None else new_workspace(dev)
+    ws = workspace if workspace is not None else rmsnorm_workspace(m, dev)
     _call("nvfp4_rmsnorm_quantize_act", _ptr(x), _ptr(gamma), m, k, x.stride(0),
           ctypes.c_float(eps), _ptr(alpha_in), _ptr(out.alpha), _ptr(out.codes),
           _ptr(out.scales), _ptr(y_out), y_out.stride(0) if y_out is not None else 0,

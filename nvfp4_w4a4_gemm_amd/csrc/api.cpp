@@ -190,6 +190,11 @@ nvfp4_status_t nvfp4_quantize_act_noalloc(const void* x_bf16, int64_t M, int64_t
                          stream, true);
 }
 
+size_t nvfp4_rmsnorm_workspace_bytes(int64_t M) {
+  if (M < 0) return 0;
+  return nvfp4::kWsRowR + 4 * (size_t)M;
+}
+
 nvfp4_status_t nvfp4_rmsnorm_quantize_act(const void* x_bf16, const void* gamma_bf16, int64_t M,
                                           int64_t K, int64_t ld_x, float eps,
                                           const float* alpha_in, float* alpha_out,
@@ -226,11 +231,15 @@ nvfp4_status_t nvfp4_rmsnorm_quantize_act(const void* x_bf16, const void* gamma_
   a.scales = scales;
   a.y_out = y_bf16;
   a.ld_y = ld_y;
+  // room for each row's r: the amax pass keeps it for the quantise pass
+  a.row_r = (alpha_in == nullptr && workspace_bytes >= nvfp4_rmsnorm_workspace_bytes(M))
+                ? reinterpret_cast<float*>(w + nvfp4::kWsRowR)
+                : nullptr;
   int n_partials = 0;
   if (alpha_in == nullptr && M > 0) {
     a.amax_pass = true;
     if (nvfp4::launch_rmsnorm_quant(a, stream) != hipSuccess) return NVFP4_ERR_LAUNCH;
-    n_partials = nvfp4::rmsnorm_amax_grid(M);
+    n_partials = nvfp4::rmsnorm_amax_grid(M, K);
   }
   if (nvfp4::launch_prepare(w + nvfp4::kWsPartials, n_partials, alpha_in, alpha_out, w, stream) !=
       hipSuccess)

@@ -21,6 +21,9 @@ constexpr int kCodeLutRow = 1024;            // BF16 x in [2^-3, 2^5)
 constexpr int kCodeLutN = 8 * kCodeLutRow;   // one row per E4M3 mantissa
 constexpr size_t kWsCodeLut = kWsSigLut + 3072;
 constexpr size_t kWorkspaceBytes = kWsCodeLut + kCodeLutN;   // 15616
+// RMSNorm + quantiser: one float a row after the quantiser's workspace
+constexpr size_t kWsRowR = 15872;
+static_assert(kWsRowR >= kWorkspaceBytes && kWsRowR % 256 == 0, "row r offset");
 
 // BF16 bit patterns of the first entries of the two tables.
 constexpr int kSigLutBase = 117 * 128;       // 2^-10
@@ -65,9 +68,11 @@ struct RmsQuantArgs {
   uint16_t* y_out;           // nullable BF16 [M][ld_y]
   int64_t ld_y;
   bool amax_pass;            // true: the amax pass, false: the quantise pass
+  float* row_r;              // nullable [M]: each row's r, written by the amax
+                             // pass, read by the segment-walk quantise pass
 };
 constexpr int64_t kRmsMaxK = 8192;
-int rmsnorm_amax_grid(int64_t M);
+int rmsnorm_amax_grid(int64_t M, int64_t K);   // workgroups (partials) of the amax pass
 hipError_t launch_rmsnorm_quant(const RmsQuantArgs& args, hipStream_t stream);
 
 // ---- GEMMs -----------------------------------------------------------------

@@ -35,7 +35,7 @@ def test_header_declares_the_four_entry_points():
     for n in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "w4a4_gemm", "bf16_gemm_baseline",
               "w4a4_gemm_multi", "w4a4_gemm_grouped", "w4a4_gemm_fused_act",
               "w4a4_gemm_decode", "nvfp4_rmsnorm_quantize_act", "w4a4_gemm_silu_mul_quantize",
-              "w4a4_gemm_silu_mul_workspace_bytes"):
+              "w4a4_gemm_silu_mul_workspace_bytes", "nvfp4_rmsnorm_workspace_bytes"):
         assert n in names
 
 
@@ -224,6 +224,18 @@ def test_gemm_decode_validation(lib):
     assert f(*bad) == SHAPE
     zero = list(args); zero[7] = 0
     assert f(*zero) == OK
+
+
+@needs_lib
+def test_rmsnorm_workspace_bytes(lib):
+    """One float a row after the quantiser's workspace (256-byte aligned
+    start), so the r of a row fits; nothing for a negative M."""
+    base = lib.nvfp4_workspace_bytes()
+    for m in (0, 1, 8192, 16384):
+        need = lib.nvfp4_rmsnorm_workspace_bytes(m)
+        assert need >= base + 4 * m and (need - 4 * m) % 256 == 0
+        assert need - 4 * m - base < 512
+    assert lib.nvfp4_rmsnorm_workspace_bytes(-1) == 0
 
 
 @needs_lib

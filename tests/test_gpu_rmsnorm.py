@@ -37,7 +37,15 @@ def check(xb, gb, eps, alpha_in=None, pool=None):
     a_in = None if alpha_in is None else torch.tensor([alpha_in], dtype=torch.float32, device=DEV)
     q = nv.nvfp4_rmsnorm_quantize_act(x, g, eps, alpha_in=a_in, y_out=y)
     q2 = nv.nvfp4_rmsnorm_quantize_act(x, g, eps, alpha_in=a_in)     # without y
+    # the quantiser's workspace alone: the quantise pass sums each row again
+    # instead of reading the r the amax pass stored; the same bits
+    y3 = torch.empty_like(y)
+    q3 = nv.nvfp4_rmsnorm_quantize_act(x, g, eps, alpha_in=a_in, y_out=y3,
+                                       workspace=nv.new_workspace(DEV))
     torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y3.view(torch.int16))
+    assert torch.equal(q.codes, q3.codes) and torch.equal(q.scales, q3.scales)
+    assert torch.equal(q.alpha, q3.alpha)
     yk = host_bits(y)
     yref = orc.rmsnorm(xb, gb, eps)[1] if pool is None else rmsnorm_all_rows(pool, xb, gb, eps)
     assert yref.shape == yk.shape
@@ -83,6 +91,27 @@ def test_rmsnorm_quantize_extreme_given_alpha(m, k, alpha_in):
     in registers (K <= 5120) and streamed (K = 6144)."""
     xb = normal_bits(m, k, seed=m + k)
     check(xb, gamma_bits(k, 3), 1e-6, alpha_in=alpha_in)
+
+
+@pytest.mark.parametrize("m,k", [(37, 2816), (70, 5120), (9, 4096)])
+def test_rmsnorm_quantize_strided_rows(m, k):
+    """x and y with row strides beyond K (views into wider rows): the same
+    codes, scales and y as the dense call, with and without the stored r."""
+    xb = normal_bits(m, k, seed=11 * m + k)
+    g = torch.from_numpy(gamma_bits(k, 4).view(np.int16)).to(DEV).view(torch.bfloat16)
+    x = dev_bf16(xb)
+    wide = torch.full((m, k + 72), 3.0, dtype=torch.bfloat16, device=DEV)
+    wide[:, :k] = x
+    y = torch.empty(m, k, dtype=torch.bfloat16, device=DEV)
+    q = nv.nvfp4_rmsnorm_quantize_act(x, g, 1e-6, y_out=y)
+    for ws in (None, nv.new_workspace(DEV)):
+        yw = torch.full((m, k + 24), 5.0, dtype=torch.bfloat16, device=DEV)
+        qs = nv.nvfp4_rmsnorm_quantize_act(wide[:, :k], g, 1e-6, y_out=yw[:, :k], workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(qs.codes, q.codes) and torch.equal(qs.scales, q.scales)
+        assert torch.equal(qs.alpha, q.alpha)
+        assert torch.equal(yw[:, :k].view(torch.int16), y.view(torch.int16))
+        assert torch.all(yw[:, k:] == 5.0)
 
 
 def test_rmsnorm_quantize_full_size():
