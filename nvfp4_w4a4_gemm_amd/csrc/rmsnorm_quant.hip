@@ -11,7 +11,8 @@
 // amax|y| / 2688), block scales and codes by the exact decision tables;
 // same digest, 方法步骤详情 step (3)).
 //
-// Two passes over x, one wave per row (the row stays in registers):
+// Two passes over x, one wave per row (the row stays in registers, gamma
+// sits in LDS as float32, unpacked once per workgroup):
 //   1. rmsnorm_amax_kernel: r and the amax of |y| per workgroup (partials);
 //   2. prepare_kernel (quantize.hip): alpha and the decision tables;
 //   3. rmsnorm_quantize_kernel: r and y again, by the same code, then codes
@@ -106,12 +107,7 @@ __device__ __forceinline__ float row_inv_rms(const Row<CH>& row, int K, float ep
 // y of one chunk (8 values, element 2i in the low half of word i).
 __device__ __forceinline__ u32x4 chunk_y(const u32x4 x, const u32x4 g, float r) {
   uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-#ifdef RMS_G_OPAQUE
-  uint32_t gw[4] = {g.x, g.y, g.z, g.w};
-  asm volatile("" : "+v"(gw[0]), "+v"(gw[1]), "+v"(gw[2]), "+v"(gw[3]));
-#else
   const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
-#endif
   // unpack the words again here rather than keep the whole row unpacked
   // from the sum of squares (which would double the row's registers)
   asm volatile("" : "+v"(xw[0]), "+v"(xw[1]), "+v"(xw[2]), "+v"(xw[3]));
@@ -128,10 +124,60 @@ __device__ __forceinline__ u32x4 chunk_y(const u32x4 x, const u32x4 g, float r) 
   return u32x4{y[0], y[1], y[2], y[3]};
 }
 
-// The wave's rows: blockIdx.x * 4 + wave, then every gridDim.x * 4 rows.  A
-// lane always touches the same chunks, so gamma is loaded once; with kPre
-// the next row's x is loaded before the current row is processed, so one
-// row's HBM round trip overlaps the other's arithmetic.
+// gamma of the held-row kernels as float32 in LDS, unpacked once per
+// workgroup: chunk c's elements 0-3 at h[0][c], 4-7 at h[1][c] (the lanes of a
+// wave read consecutive 16-byte slots, so no bank conflicts).  Chunks past
+// the row's end hold zeros.
+template <int CH>
+struct GammaLds {
+  float4_t h[2][64 * CH];
+};
+
+template <int CH>
+__device__ __forceinline__ void fill_gamma(const uint16_t* __restrict__ gamma, int nc,
+                                           GammaLds<CH>& gl) {
+  const u32x4* g4 = reinterpret_cast<const u32x4*>(gamma);
+  for (int c = threadIdx.x; c < 64 * CH; c += kThreads) {
+    const u32x4 g = c < nc ? g4[c] : u32x4{0u, 0u, 0u, 0u};
+    gl.h[0][c] = float4_t{__uint_as_float(g.x << 16), __uint_as_float(g.x & 0xFFFF0000u),
+                          __uint_as_float(g.y << 16), __uint_as_float(g.y & 0xFFFF0000u)};
+    gl.h[1][c] = float4_t{__uint_as_float(g.z << 16), __uint_as_float(g.z & 0xFFFF0000u),
+                          __uint_as_float(g.w << 16), __uint_as_float(g.w & 0xFFFF0000u)};
+  }
+}
+
+// The float32 values (x * r) * gamma of one chunk (the same arithmetic as
+// chunk_y, before the rounding to BF16), gamma from LDS.
+struct Chunk8f {
+  float v[8];
+};
+__device__ __forceinline__ Chunk8f chunk_xrg(const u32x4 x, const float4_t ga, const float4_t gb,
+                                             float r) {
+  uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+  asm volatile("" : "+v"(xw[0]), "+v"(xw[1]), "+v"(xw[2]), "+v"(xw[3]));
+  const float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+  Chunk8f o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o.v[2 * i] = (__uint_as_float(xw[i] << 16) * r) * g[2 * i];
+    o.v[2 * i + 1] = (__uint_as_float(xw[i] & 0xFFFF0000u) * r) * g[2 * i + 1];
+  }
+  return o;
+}
+
+__device__ __forceinline__ u32x4 to_bf16x8(const Chunk8f& f) {
+  uint32_t y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    y[i] = __builtin_bit_cast(uint32_t,
+                              __builtin_convertvector((float2_t){f.v[2 * i], f.v[2 * i + 1]},
+                                                      bf16x2_t));
+  return u32x4{y[0], y[1], y[2], y[3]};
+}
+
+// The wave's rows: blockIdx.x * 4 + wave, then every gridDim.x * 4 rows.
+// With kPre the next row's x is loaded before the current row is processed,
+// so one row's HBM round trip overlaps the other's arithmetic.
 // `first(load)` runs once and must call load() (which issues the first
 // row's loads); the quantise pass issues its table loads before it.  Every
 // wave of the workgroup runs it, also a wave without a row.
@@ -172,43 +218,50 @@ __device__ __forceinline__ void for_rows(const uint16_t* __restrict__ x, int M, 
   }
 }
 
-template <int CH, bool kFull>
-__device__ __forceinline__ void load_gamma(const uint16_t* __restrict__ gamma, int nc, int lane,
-                                           u32x4 (&g)[CH]) {
-  const u32x4* g4 = reinterpret_cast<const u32x4*>(gamma);
-#pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    const int c = lane + 64 * j;
-    g[j] = kFull || c < nc ? g4[c] : u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
 // row_r (nullable): each row's r, for rmsnorm_quantize_seg_kernel.
-#ifdef RMS_AMAX_W4
-#define RMS_AMAX_ATTR __attribute__((amdgpu_waves_per_eu(4)))
-#else
-#define RMS_AMAX_ATTR
-#endif
 template <int CH, bool kPre, bool kFull>
-__global__ __launch_bounds__(kThreads) RMS_AMAX_ATTR void rmsnorm_amax_kernel(
+__global__ __launch_bounds__(kThreads) void rmsnorm_amax_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, int M, int K,
     int64_t ld_x, float eps, uint32_t* __restrict__ partials, float* __restrict__ row_r) {
+  __shared__ GammaLds<CH> gl;
   const int lane = threadIdx.x & 63;
   const int nc = K / 8;
-  u32x4 g[CH];
-  load_gamma<CH, kFull>(gamma, nc, lane, g);
-  uint32_t m = 0;
-  for_rows<CH, kPre, kFull>(x, M, nc, ld_x, lane, [](auto load) { load(); }, [&](int rowi, const Row<CH>& row) {
+  uint32_t m = 0;       // BF16 magnitude bits (rows whose r is not finite)
+  float mf = 0.0f;      // float32 magnitudes (every other row)
+  auto first = [&](auto load) {
+    load();
+    fill_gamma<CH>(gamma, nc, gl);
+    __syncthreads();
+  };
+  for_rows<CH, kPre, kFull>(x, M, nc, ld_x, lane, first, [&](int rowi, const Row<CH>& row) {
     const float r = row_inv_rms<CH>(row, K, eps);
     if (row_r != nullptr && lane == 0) row_r[rowi] = r;
+    if (__builtin_isfinite(r)) {
+      // |y| = RNE_bf16(|(x r) gamma|) and the rounding is monotonic, so the
+      // largest |y| is the rounding of the largest float32 magnitude
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const u32x4 y = chunk_y(row.x[j], g[j], r);      // zero past the row end
-      m = pk_max_u16(m, pk_max_u16(pk_max_u16(y.x & 0x7FFF7FFFu, y.y & 0x7FFF7FFFu),
-                                   pk_max_u16(y.z & 0x7FFF7FFFu, y.w & 0x7FFF7FFFu)));
+      for (int j = 0; j < CH; ++j) {
+        const int c = lane + 64 * j;
+        const Chunk8f f = chunk_xrg(row.x[j], gl.h[0][c], gl.h[1][c], r);   // zero past the end
+#pragma unroll
+        for (int i = 0; i < 8; i += 2)
+          mf = __builtin_fmaxf(mf, __builtin_fmaxf(__builtin_fabsf(f.v[i]), __builtin_fabsf(f.v[i + 1])));
+      }
+    } else {
+      // r = inf (eps = 0 and a row whose squares sum to 0): the BF16 values
+      // themselves, so that a NaN y (0 * inf) reaches alpha as it would
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int c = lane + 64 * j;
+        const u32x4 y = to_bf16x8(chunk_xrg(row.x[j], gl.h[0][c], gl.h[1][c], r));
+        m = pk_max_u16(m, pk_max_u16(pk_max_u16(y.x & 0x7FFF7FFFu, y.y & 0x7FFF7FFFu),
+                                     pk_max_u16(y.z & 0x7FFF7FFFu, y.w & 0x7FFF7FFFu)));
+      }
     }
   });
   m = max(m & 0xFFFFu, m >> 16);
+  m = max(m, __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){mf, 0.0f}, bf16x2_t)) &
+                 0xFFFFu);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
   __shared__ uint32_t red[kRowsPerBlock];
@@ -340,13 +393,8 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quantize_stream_kernel(
                            fast_tables(tl, P), P.slow != 0, codes, scales, y_out, ld_y);
 }
 
-#ifdef RMS_Q_W3
-#define RMS_Q_ATTR __attribute__((amdgpu_waves_per_eu(3)))
-#else
-#define RMS_Q_ATTR
-#endif
 template <int CH, bool kPre, bool kFull>
-__global__ __launch_bounds__(kThreads) RMS_Q_ATTR void rmsnorm_quantize_kernel(
+__global__ __launch_bounds__(kThreads) void rmsnorm_quantize_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, int M, int K,
     int64_t ld_x, float eps, const uint8_t* __restrict__ ws, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, uint16_t* __restrict__ y_out, int64_t ld_y) {
@@ -364,11 +412,11 @@ __global__ __launch_bounds__(kThreads) RMS_Q_ATTR void rmsnorm_quantize_kernel(
                              fast_tables(tl, P), true, codes, scales, y_out, ld_y);
     return;
   }
-  u32x4 g[CH];
-  load_gamma<CH, kFull>(gamma, nc, lane, g);
+  __shared__ GammaLds<CH> gl;
   // the tables' loads go first, then the first row's (see copy_tables_first)
   auto tables = [&](auto load) {
     copy_tables_first(ws, tl, threadIdx.x, load);
+    fill_gamma<CH>(gamma, nc, gl);
     __syncthreads();
   };
   for_rows<CH, kPre, kFull>(x, M, nc, ld_x, lane, tables, [&](int rowi, const Row<CH>& row) {
@@ -379,11 +427,11 @@ __global__ __launch_bounds__(kThreads) RMS_Q_ATTR void rmsnorm_quantize_kernel(
       // lanes 2i and 2i + 1 hold the two halves of a block (64 is even);
       // every lane of the wave takes part in the exchange (past the row's
       // end the values are zero and nothing is stored)
-      const u32x4 y = chunk_y(row.x[j], g[j], r);
+      const int c = lane + 64 * j;
+      const u32x4 y = to_bf16x8(chunk_xrg(row.x[j], gl.h[0][c], gl.h[1][c], r));
       const uint32_t w[4] = {y.x, y.y, y.z, y.w};
       uint32_t sb;
       const uint32_t o = quantize_half_block(w, t, sb);
-      const int c = lane + 64 * j;
       if (kFull || c < nc) {
         reinterpret_cast<uint32_t*>(codes + (int64_t)rowi * (K / 2))[c] = o;
         if ((lane & 1) == 0) (scales + (int64_t)rowi * (K / 16))[c >> 1] = (uint8_t)sb;
@@ -529,42 +577,21 @@ hipError_t launch_stream(const RmsQuantArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-#ifdef RMS_AMAX_NOPRE
-constexpr bool kAmaxPre = false;
-#else
-constexpr bool kAmaxPre = true;
-#endif
-#ifdef RMS_Q_NOPRE
-constexpr bool kQPre = false;
-#else
-constexpr bool kQPre = true;
-#endif
-
 template <int CH, bool kFull>
 int amax_grid_ch(int64_t M) {
   const int64_t blocks = (M + kRowsPerBlock - 1) / kRowsPerBlock;
-#ifdef RMS_AMAX_NOFIT
-  const int64_t cap = kAmaxPartials;
-#else
   // as many workgroups as fit at once, so that no second, partial wave of
-  // workgroups follows
-  int64_t cap = resident_blocks<rmsnorm_amax_kernel<CH, kAmaxPre && CH <= 10, kFull>>();
+  // workgroups follows (measured 5% faster at 8192 x 4096 and 16384 x 5120)
+  int64_t cap = resident_blocks<rmsnorm_amax_kernel<CH, (CH <= 10), kFull>>();
   if (cap > kAmaxPartials) cap = kAmaxPartials;
-#endif
   return (int)(blocks < cap ? blocks : cap);
 }
 
 template <int CH, bool kFull>
 hipError_t launch_ch_full(const RmsQuantArgs& a, hipStream_t stream) {
-  // two rows held (the next one loading) where registers allow; the
-  // quantise pass at CH = 8 holds one (fewer registers: three waves a SIMD
-  // instead of two, measured 4% faster at 8192 x 4096)
-#ifdef RMS_Q_PRE8
-  constexpr bool kPre = kQPre && CH <= 10;
-#else
-  constexpr bool kPre = kQPre && CH <= 10 && CH != 8;
-#endif
-  constexpr bool kPreA = kAmaxPre && CH <= 10;
+  // two rows held (the next one loading) where registers allow
+  constexpr bool kPre = CH <= 10;
+  constexpr bool kPreA = CH <= 10;
   const int64_t blocks = (a.M + kRowsPerBlock - 1) / kRowsPerBlock;
   if (a.amax_pass) {
     const int grid = amax_grid_ch<CH, kFull>(a.M);
