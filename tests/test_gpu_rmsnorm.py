@@ -93,6 +93,27 @@ def test_rmsnorm_quantize_extreme_given_alpha(m, k, alpha_in):
     check(xb, gamma_bits(k, 3), 1e-6, alpha_in=alpha_in)
 
 
+@pytest.mark.parametrize("k", [4096, 2816])
+def test_rmsnorm_quantize_zero_row_without_eps(k):
+    """eps = 0 and a row of zeros: r = 1/sqrt(0) is infinite and that row's y
+    is 0 * inf = NaN by the definition, so alpha is NaN (the amax pass takes
+    such rows through BF16 bit patterns, in which NaN is the largest); the
+    other rows' y are unaffected."""
+    m = 12
+    xb = normal_bits(m, k, seed=k)
+    xb[5] = 0
+    g = torch.from_numpy(gamma_bits(k, 2).view(np.int16)).to(DEV).view(torch.bfloat16)
+    y = torch.empty(m, k, dtype=torch.bfloat16, device=DEV)
+    q = nv.nvfp4_rmsnorm_quantize_act(dev_bf16(xb), g, 0.0, y_out=y)
+    torch.cuda.synchronize()
+    assert torch.isnan(q.alpha).all()
+    assert torch.isnan(y[5].float()).all()
+    yk = host_bits(y)
+    yref = orc.rmsnorm(np.delete(xb, 5, axis=0), gamma_bits(k, 2), 0.0)[1]
+    d = np.abs(bf16_ordered(np.delete(yk, 5, axis=0)) - bf16_ordered(yref))
+    assert d.max() <= 1
+
+
 @pytest.mark.parametrize("m,k", [(37, 2816), (70, 5120), (9, 4096)])
 def test_rmsnorm_quantize_strided_rows(m, k):
     """x and y with row strides beyond K (views into wider rows): the same
