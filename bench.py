@@ -430,10 +430,87 @@ def main():
                                                      args.steps, 3, hidden=25600, std=0.015)
         log("timing decode-shaped W4A4 GEMMs (w4a4_gemm_decode) against hipBLASLt BF16")
         result["decode"] = decode_block(nv, torch, dev, workspace, args.steps, 3)
+        log("timing the layer with its producers (RMSNorm, SiLU*up) on both sides")
+        result["layer_with_producers"] = producers_block(nv, torch, dev, x_dev, w_dev, wq,
+                                                         qbuf, workspace, args)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows, args.cpu_cols, m)
     print(json.dumps(result), flush=True)
+
+
+def producers_block(nv, torch, dev, x_dev, w_dev, wq, qbuf, workspace, args):
+    """The same four projections with the operations that produce their
+    inputs in a transformer block, on both sides: RMSNorm before Q|K|V and
+    before gate|up, and H = SiLU(gate) * up between gate|up and down (the
+    attention that produces O's input is not part of either side; X_o is
+    given).  W4A4: nvfp4_rmsnorm_quantize_act for the two normalised inputs,
+    the gate|up GEMM with SiLU*up and H's quantiser fused in
+    (w4a4_gemm_silu_mul_quantize, gate and up rows interleaved), the
+    quantiser for X_o, and the W4A4 GEMMs.  BF16: torch rms_norm, torch.matmul
+    (hipBLASLt) and torch silu and multiply.  The GEMM FLOPs are the same on
+    both sides."""
+    m, hid = x_dev["X_qkv"].shape
+    inter = w_dev["W_down"].shape[1]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    g1, g2 = [(1.0 + 0.1 * torch.randn(hid, device=dev, generator=gen)).to(torch.bfloat16)
+              for _ in range(2)]
+    wgu = w_dev["W_gu"]
+    qg = nv.nvfp4_quantize_weights(wgu[:inter].contiguous(), workspace=workspace)
+    qu = nv.nvfp4_quantize_weights(wgu[inter:].contiguous(), workspace=workspace)
+    stack = nv.interleave_gate_up(qg, qu)
+    del qg, qu
+    ws_silu = nv.silu_mul_workspace(m, 2 * inter, dev)
+    ws_norm = nv.rmsnorm_workspace(m, dev)
+    qn1 = nv.nvfp4_rmsnorm_quantize_act(x_dev["X_qkv"], g1, 1e-6, workspace=ws_norm)
+    qn2 = nv.nvfp4_rmsnorm_quantize_act(x_dev["X_gu"], g2, 1e-6, workspace=ws_norm)
+    qh, h = nv.w4a4_gemm_silu_mul_quantize(qn2, stack, workspace=ws_silu)
+    y = {name: torch.empty(m, w_dev[wname].shape[0], dtype=torch.bfloat16, device=dev)
+         for _, wname, name in LAYER if name != "gate_up"}
+    torch.cuda.synchronize()
+
+    def w4a4(i):
+        nv.nvfp4_rmsnorm_quantize_act(x_dev["X_qkv"], g1, 1e-6, out=qn1, workspace=ws_norm)
+        nv.w4a4_gemm(qn1, wq["W_qkv"], f32=False, y_bf16=y["qkv"])
+        nv.nvfp4_quantize_act(x_dev["X_o"], out=qbuf["X_o"], workspace=workspace)
+        nv.w4a4_gemm(qbuf["X_o"], wq["W_o"], f32=False, y_bf16=y["o"])
+        nv.nvfp4_rmsnorm_quantize_act(x_dev["X_gu"], g2, 1e-6, out=qn2, workspace=ws_norm)
+        nv.w4a4_gemm_silu_mul_quantize(qn2, stack, h=h, out=qh, workspace=ws_silu)
+        nv.w4a4_gemm(qh, wq["W_down"], f32=False, y_bf16=y["down"])
+
+    def bf16(i):
+        a = torch.nn.functional.rms_norm(x_dev["X_qkv"], (hid,), g1, 1e-6)
+        torch.matmul(a, w_dev["W_qkv"].t())
+        torch.matmul(x_dev["X_o"], w_dev["W_o"].t())
+        b = torch.nn.functional.rms_norm(x_dev["X_gu"], (hid,), g2, 1e-6)
+        gu = torch.matmul(b, wgu.t())
+        hb = torch.nn.functional.silu(gu[:, :inter]) * gu[:, inter:]
+        del gu
+        torch.matmul(hb, w_dev["W_down"].t())
+
+    def run(fn):
+        settle_with(torch, fn, args.settle_ms)
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(args.steps):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e3 / args.steps
+
+    tw = run(w4a4)
+    tb = run(bf16)
+    flops = sum(2.0 * m * w_dev[wname].shape[0] * w_dev[wname].shape[1] for _, wname, _ in LAYER)
+    log(f"layer with producers: W4A4 {tw:.3f} ms ({flops / (tw * 1e-3) / 1e12:.0f} TFLOP/s), "
+        f"BF16 hipBLASLt + torch {tb:.3f} ms; x{tb / tw:.3f}")
+    return {"w4a4_ms_per_step": round(tw, 4), "bf16_hipblaslt_torch_ms_per_step": round(tb, 4),
+            "gemm_tflops_w4a4": round(flops / (tw * 1e-3) / 1e12, 1),
+            "speedup_vs_bf16": round(tb / tw, 3),
+            "w4a4_ops": "rmsnorm+quantise, QKV GEMM, quantise X_o, O GEMM, rmsnorm+quantise, "
+                        "gate|up GEMM with SiLU*up and H's quantiser, down GEMM",
+            "bf16_ops": "torch rms_norm, matmul, matmul, rms_norm, matmul, silu*mul, matmul"}
 
 
 def attention_block(nv, torch, dev, workspace, args):
