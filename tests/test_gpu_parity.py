@@ -485,6 +485,43 @@ def test_w4a4_gemm_persistent_equals_grid(m, n, k, out):
         assert_gemm_close(None, y_p[1][rows], y, bound, y16_ref)
 
 
+@pytest.mark.parametrize("gather", [False, True])
+def test_grouped_gemm_many_tiles(gather):
+    """A grouped GEMM of several windows of 256 tiles (the tile order the
+    grouped launch uses within each window): groups of ragged sizes, empty
+    ones among them, with and without a row gather; one row of every 256-row
+    tile of every group (and each group's last row) against the oracle over
+    all columns, so every tile is checked."""
+    rng = np.random.default_rng(77 + gather)
+    g, n, k, tokens = 9, 4096, 512, 6000
+    counts = np.array([2100, 0, 1777, 256, 3001, 0, 1, 4000, 2500])
+    m = int(counts.sum())
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    row_index = rng.integers(0, tokens, size=m).astype(np.int32) if gather else None
+    xb = normal_bits(tokens if gather else m, k, seed=78)
+    wbs = [normal_bits(n, k, seed=80 + e, std=0.02, outliers=False) for e in range(g)]
+    qa = nv.nvfp4_quantize_act(dev_bf16(xb))
+    qws = [nv.nvfp4_quantize_weights(dev_bf16(w)) for w in wbs]
+    b_codes = torch.stack([q.codes for q in qws])
+    b_scales = torch.stack([q.scales for q in qws])
+    b_alpha = torch.cat([q.alpha for q in qws])
+    off_t = torch.from_numpy(offsets).to(DEV)
+    idx_t = torch.from_numpy(row_index).to(DEV) if gather else None
+    y16 = nv.w4a4_gemm_grouped(qa, b_codes, b_scales, b_alpha, off_t, a_row_index=idx_t,
+                               f32=False)[1]
+    torch.cuda.synchronize()
+    ra = orc.quantize(xb)
+    for e in range(g):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if lo == hi:
+            continue
+        rows = np.unique(np.concatenate([np.arange(lo + 97 % (hi - lo), hi, 256), [hi - 1]]))
+        src = row_index[rows] if gather else rows
+        y, bound, y16_ref = orc.w4a4_reference((ra[0], ra[1][src], ra[2][src]),
+                                               orc.quantize(wbs[e]))
+        assert_gemm_close(None, y16[torch.from_numpy(rows).to(DEV)], y, bound, y16_ref)
+
+
 def test_w4a4_gemm_multi_persistent_equals_grid():
     m, k = 8192, 512
     parts = [normal_bits(n, k, seed=90 + i, std=std, outliers=False)
