@@ -11,9 +11,10 @@
 //
 // At this shape the work is a stream over the weight codes (0.5625 bytes a
 // weight): the kernel is bound by HBM, not by the matrix cores.  One token
-// row (with K % 32 == 0, K <= 8192) takes the matrix-vector kernel
-// w4a4_gemv_kernel (whole weight rows a wave, described there); otherwise
-// the layout is:
+// row (with K % 32 == 0) takes a matrix-vector kernel: w4a4_gemv_kernel
+// (K <= 8192, whole weight rows a wave) or w4a4_gemv_split_kernel
+// (K <= 32768, each row's K split over the four waves of a workgroup), both
+// described there; otherwise the layout is:
 //
 //  - A workgroup (4 waves) owns 16 output columns and all of K.  The K axis
 //    is cut into 32-element chunks (16 code bytes and 2 scale bytes a row);
@@ -671,107 +672,116 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemv_kernel(
   }
 }
 
-// The same product for longer rows (K up to 32768): the token's values,
-// decoded once per workgroup, sit in LDS (2 bytes a value) instead of
-// registers, and a wave walks its rows' chunks in rounds of kR a lane, the
-// next round's loads in flight while a round is used.
-constexpr int kGemvLdsMaxK = 32768;
-template <int kR>
-__global__ __launch_bounds__(kThreads) void w4a4_gemv_lds_kernel(
+// The same product for long rows (8192 < K <= 32768) with the token in
+// registers: the four waves of a workgroup split each row's chunks into four
+// contiguous parts (wave w the w-th, up to 64 CH chunks), and each wave keeps
+// the token's values of its part decoded in registers, as w4a4_gemv_kernel
+// does for a whole row.  A workgroup walks rows b, b + gridDim.x, ...; each
+// wave sums its part of a row as w4a4_gemv_kernel sums a row (exact block
+// sums times sigma_w, a fixed-order DPP reduction) and leaves the partial
+// in LDS; after every kSplitRows rows (and the last) one barrier, then the
+// four partials of each row are added in a fixed order (part 0 + 1 + 2 + 3)
+// and scaled.  The partials alternate between two LDS buffers, so one
+// barrier a batch suffices.
+constexpr int kSplitRows = 8;
+constexpr int kGemvSplitMaxK = 4 * 64 * 32 * 4;     // 32768
+template <int CH>
+__global__ __launch_bounds__(kThreads) void w4a4_gemv_split_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ alpha_a, const uint8_t* __restrict__ b_codes,
     const uint8_t* __restrict__ b_scales, const float* __restrict__ alpha_b,
     const float* __restrict__ alpha_b_rows, int N, int K, float* __restrict__ y_f32,
     uint16_t* __restrict__ y_bf16) {
-  // pair k (0..15) of chunk c at av[k nc + c]: the lanes of a wave read
-  // consecutive words
-  extern __shared__ half2_t av[];
+  __shared__ float part[2][kSplitRows][kWaves];
   const int lane = threadIdx.x & 63;
-  const int nc = K / 32;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nc = K / 32;                              // chunks a row
+  const int per = (nc + kWaves - 1) / kWaves;         // chunks a part (<= 64 CH)
+  const int c0 = wave * per;
+  const int c_end = c0 + per < nc ? c0 + per : nc;    // c0 < c_end: nc >= 4
   const uint32_t row_codes = (uint32_t)(K / 2), row_scales = (uint32_t)(K / 16);
   const __amdgpu_buffer_rsrc_t rbc = buffer_of(b_codes, (uint32_t)N * row_codes);
   const __amdgpu_buffer_rsrc_t rbs = buffer_of(b_scales, (uint32_t)N * row_scales);
-  for (int c = threadIdx.x; c < nc; c += kThreads) {
-    const u32x4 w = reinterpret_cast<const u32x4*>(a_codes)[c];
-    const uint32_t sb = reinterpret_cast<const uint16_t*>(a_scales)[c];
+
+  // the token's values of this lane's chunks of the part (zero past its end)
+  half2_t av[CH][16];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int c = c0 + lane + 64 * j;
+    const bool ok = c < c_end;
+    const u32x4 w = ok ? reinterpret_cast<const u32x4*>(a_codes)[c] : u32x4{0u, 0u, 0u, 0u};
+    const uint32_t sb = ok ? (uint32_t)reinterpret_cast<const uint16_t*>(a_scales)[c] : 0u;
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const half2_t s = scale_pair((sb >> (8 * (q >> 1))) & 0xFFu);
       const Half2x4 v = cvt8(ww[q], 16.0f);
 #pragma unroll
-      for (int h = 0; h < 4; ++h) av[(4 * q + h) * nc + c] = v.h[h] * s;
+      for (int h = 0; h < 4; ++h) av[j][4 * q + h] = v.h[h] * s;
     }
   }
-  __syncthreads();
-  const float scale_a = (*alpha_a) * 4096.0f;
-  const int wstride = (int)gridDim.x * kWaves;
-  // the wave's work: rows n0, n0 + wstride, ..., each in `rounds` rounds;
-  // item i = (row n0 + (i / rounds) wstride, round i % rounds).  The next
-  // item's loads are issued before an item is used.
-  const int rounds = (nc + 64 * kR - 1) / (64 * kR);
-  const int n0 = (int)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int my_rows = n0 < N ? (N - 1 - n0) / wstride + 1 : 0;
-  const int items = my_rows * rounds;
-  struct Item {
-    u32x4 codes[kR];
-    uint32_t sc[kR];
+
+  struct RowData {
+    u32x4 codes[CH];
+    uint32_t scales[CH];
   };
-  auto load = [&](int i, Item& d) __attribute__((always_inline)) {
-    const int ic = i < items ? i : items - 1;          // clamped: always valid
-    const uint32_t n = (uint32_t)(n0 + (ic / rounds) * wstride);
-    const int c0 = (ic % rounds) * 64 * kR;
+  auto load_row = [&](int n, RowData& d) __attribute__((always_inline)) {
+    const uint32_t rn = (uint32_t)(n < N ? n : N - 1);          // clamped: loads always valid
 #pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      const int c = c0 + lane + 64 * r;
-      const uint32_t cc = (uint32_t)(c < nc ? c : nc - 1);
-      d.codes[r] = __builtin_amdgcn_raw_buffer_load_b128(rbc, n * row_codes + 16u * cc, 0, 2);
-      d.sc[r] = __builtin_amdgcn_raw_buffer_load_b16(rbs, n * row_scales + 2u * cc, 0, 0);
+    for (int j = 0; j < CH; ++j) {
+      const int c = c0 + lane + 64 * j;
+      const uint32_t cc = (uint32_t)(c < c_end ? c : c_end - 1);
+      d.codes[j] = __builtin_amdgcn_raw_buffer_load_b128(rbc, rn * row_codes + 16u * cc, 0, 2);
+      d.scales[j] = __builtin_amdgcn_raw_buffer_load_b16(rbs, rn * row_scales + 2u * cc, 0, 0);
     }
   };
-  Item cur, nxt;
-  if (items > 0) load(0, cur);
-  float acc = 0.0f;
-  for (int i = 0; i < items; ++i) {
-    load(i + 1, nxt);
-    const int c0 = (i % rounds) * 64 * kR;
+  const int step = (int)gridDim.x;
+  const int n0 = (int)blockIdx.x;
+  const int rows = n0 < N ? (N - n0 + step - 1) / step : 0;     // rows of this workgroup
+  RowData cur;
+  load_row(n0, cur);
+  const float scale_a = (*alpha_a) * 4096.0f;
+  for (int t = 0; t < rows; ++t) {
+    float acc = 0.0f;
 #pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      const int c = c0 + lane + 64 * r;
-      const int cc = c < nc ? c : nc - 1;
-      const uint32_t ww[4] = {cur.codes[r].x, cur.codes[r].y, cur.codes[r].z, cur.codes[r].w};
+    for (int j = 0; j < CH; ++j) {
+      const int c = c0 + lane + 64 * j;
+      const uint32_t ww[4] = {cur.codes[j].x, cur.codes[j].y, cur.codes[j].z, cur.codes[j].w};
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < 2; ++b) {                    // the chunk's two blocks
         float p = 0.0f;
 #pragma unroll
         for (int q = 2 * b; q < 2 * b + 2; ++q) {
           const Half2x4 wq = cvt8(ww[q], 1.0f);
 #pragma unroll
-          for (int h = 0; h < 4; ++h) p = __builtin_amdgcn_fdot2(wq.h[h], av[(4 * q + h) * nc + cc], p, false);
+          for (int h = 0; h < 4; ++h) p = __builtin_amdgcn_fdot2(wq.h[h], av[j][4 * q + h], p, false);
         }
-        const uint32_t sb = c < nc ? (cur.sc[r] >> (8 * b)) & 0xFFu : 0u;
+        const uint32_t sb = c < c_end ? (cur.scales[j] >> (8 * b)) & 0xFFu : 0u;
         const float sw = (float)__builtin_bit_cast(_Float16, (uint16_t)(sb << 7));
         acc = __builtin_fmaf(p, sw, acc);
       }
     }
-    if (i % rounds == rounds - 1) {
-      // the row's last round: lane 63 ends with the sum (gfx9 DPP reduction)
-      acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0xB1, 0xF, 0xF, false));
-      acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x4E, 0xF, 0xF, false));
-      acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x141, 0xF, 0xF, false));
-      acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x140, 0xF, 0xF, false));
-      acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x142, 0xA, 0xF, false));
-      acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x143, 0xC, 0xF, false));
-      const int n = n0 + (i / rounds) * wstride;
-      if (lane == 63) {
-        const float ab = alpha_b_rows != nullptr ? alpha_b_rows[n] : *alpha_b;
-        const float v = acc * (scale_a * ab);
+    // the next row's loads while this row is reduced
+    load_row(n0 + (t + 1) * step, cur);
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0xB1, 0xF, 0xF, false));
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x4E, 0xF, 0xF, false));
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x141, 0xF, 0xF, false));
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x140, 0xF, 0xF, false));
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x142, 0xA, 0xF, false));
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0x143, 0xC, 0xF, false));
+    const int slot = t % kSplitRows, buf = (t / kSplitRows) & 1;
+    if (lane == 63) part[buf][slot][wave] = acc;
+    if (slot == kSplitRows - 1 || t == rows - 1) {
+      __syncthreads();
+      if (wave == 0 && lane <= slot) {
+        const int n = n0 + (t - slot + lane) * step;
+        const float* q = part[buf][lane];
+        const float v = (((q[0] + q[1]) + q[2]) + q[3]) *
+                        (scale_a * (alpha_b_rows != nullptr ? alpha_b_rows[n] : *alpha_b));
         if (y_f32 != nullptr) y_f32[n] = v;
         if (y_bf16 != nullptr) y_bf16[n] = (uint16_t)f32_to_bf16_bits(v);
       }
-      acc = 0.0f;
     }
-    cur = nxt;
   }
 }
 
@@ -907,21 +917,34 @@ hipError_t launch_w4a4_decode(const DecodeArgs& p, hipStream_t stream) {
     if (ch <= 3) return launch_gemv<3>(p, stream);
     return launch_gemv<4>(p, stream);
   }
-  if (p.M == 1 && p.K % 32 == 0 && p.K <= kGemvLdsMaxK && (path_flags() & kPathDecodeDirect) == 0) {
-    // every workgroup resident at once (its LDS holds the token), with at
-    // least two rows a wave
-    const int lds_bytes = (int)(p.K / 32) * 64;         // 32 float16 values a chunk
-    int per_cu = (160 * 1024) / (lds_bytes + 1024);
-    per_cu = per_cu < 1 ? 1 : (per_cu > 8 ? 8 : per_cu);
-    int64_t wgs = (p.N + 2 * kWaves - 1) / (2 * kWaves);
-    const int64_t cap = (int64_t)device_cus() * per_cu;
-    if (wgs > cap) wgs = cap;
-    // 4 chunks a lane and round (measured faster at 5120 x 25600 than a
-    // whole row a round: fewer registers, more waves)
-    hipLaunchKernelGGL(w4a4_gemv_lds_kernel<4>, dim3((unsigned)wgs), dim3(kThreads), lds_bytes,
-                       stream, p.a_codes, p.a_scales, p.alpha_a, p.b_codes, p.b_scales,
-                       p.alpha_b, p.alpha_b_rows, (int)p.N, (int)p.K, p.y_f32, p.y_bf16);
-    return hipGetLastError();
+  if (p.M == 1 && p.K % 32 == 0 && p.K <= kGemvSplitMaxK && (path_flags() & kPathDecodeDirect) == 0) {
+    // four parts of at most 4 chunks a lane each; every workgroup resident
+    // (measured 21.8 -> 17.3 us at 5120 x 25600 and 10.5 -> 8.1 us at
+    // 4096 x 12288 against the token held in LDS; for rows up to 8192 the
+    // whole-row kernel above stays faster: 24576 x 4096 12.7 against 17.2 us)
+    const int64_t ch = (p.K / 32 + 4 * 64 - 1) / (4 * 64);
+    auto go = [&](auto kernel) {
+      static std::atomic<int> fit_cache[64];
+      int dev = 0;
+      (void)hipGetDevice(&dev);
+      int fit = fit_cache[dev & 63].load(std::memory_order_relaxed);
+      if (fit == 0) {
+        int occ = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0) != hipSuccess ||
+            occ < 1)
+          occ = 1;
+        fit = occ * device_cus();
+        fit_cache[dev & 63].store(fit, std::memory_order_relaxed);
+      }
+      const int64_t wgs = p.N < fit ? p.N : fit;
+      hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(kThreads), 0, stream, p.a_codes,
+                         p.a_scales, p.alpha_a, p.b_codes, p.b_scales, p.alpha_b, p.alpha_b_rows,
+                         (int)p.N, (int)p.K, p.y_f32, p.y_bf16);
+      return hipGetLastError();
+    };
+    if (ch <= 2) return go(w4a4_gemv_split_kernel<2>);
+    if (ch <= 3) return go(w4a4_gemv_split_kernel<3>);
+    return go(w4a4_gemv_split_kernel<4>);
   }
   if (p.M <= 16) return launch_mt<1>(p, stream);
   if (p.M <= 32) return launch_mt<2>(p, stream);
