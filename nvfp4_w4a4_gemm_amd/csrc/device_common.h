@@ -37,6 +37,25 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return lo | (hi << 16);
 }
 
+// Maximum of v over the 64 lanes of a wave, the same value on every lane:
+// DPP steps in a fixed order (pairs, quads, half rows, rows of 16, then rows
+// 0+1 and 0+1+2+3 by row broadcasts 15 and 31; lane 63 ends with it), all in
+// the VALU with no LDS round trip, then lane 63's value to every lane.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  // lanes of rows outside kRowMask take max(v, 0) = v
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, false));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_u32<0xB1, 0xF>(v);     // quad_perm [1,0,3,2]
+  v = dpp_max_u32<0x4E, 0xF>(v);     // quad_perm [2,3,0,1]
+  v = dpp_max_u32<0x141, 0xF>(v);    // row_half_mirror
+  v = dpp_max_u32<0x140, 0xF>(v);    // row_mirror
+  v = dpp_max_u32<0x142, 0xA>(v);    // row_bcast:15 into rows 1 and 3
+  v = dpp_max_u32<0x143, 0xC>(v);    // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Round-to-nearest-even float32 -> BF16 bits (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);

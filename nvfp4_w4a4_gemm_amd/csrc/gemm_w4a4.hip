@@ -810,8 +810,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
     else
       silu_epilogue(std::false_type{});
     uint32_t hmax = max((uint32_t)hm2[0], (uint32_t)hm2[1]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) hmax = max(hmax, (uint32_t)__shfl_xor((int)hmax, off));
+    hmax = wave_max_u32(hmax);
     __shared__ uint32_t hred[4];
     if (lane_e == 0) hred[wave] = hmax;
     __syncthreads();

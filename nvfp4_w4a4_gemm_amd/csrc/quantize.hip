@@ -103,8 +103,7 @@ __device__ __forceinline__ uint32_t chunk_amax_bits(u32x4 v) {
 
 // Writes the workgroup's maximum of m to partials[blockIdx.x].
 __device__ __forceinline__ void store_partial(uint32_t m, uint32_t* __restrict__ partials) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  m = wave_max_u32(m);
   __shared__ uint32_t red[kThreads / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -204,8 +203,7 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(
   } else {
     uint32_t m = 0;
     for (int i = threadIdx.x; i < n_partials; i += kThreads) m = max(m, partials[i]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    m = wave_max_u32(m);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     m = red[0];

@@ -262,8 +262,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_amax_kernel(
   m = max(m & 0xFFFFu, m >> 16);
   m = max(m, __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){mf, 0.0f}, bf16x2_t)) &
                  0xFFFFu);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  m = wave_max_u32(m);
   __shared__ uint32_t red[kRowsPerBlock];
   if (lane == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -321,8 +320,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_amax_stream_kernel(
     }
   }
   m = max(m & 0xFFFFu, m >> 16);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  m = wave_max_u32(m);
   __shared__ uint32_t red[kRowsPerBlock];
   if (lane == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
