@@ -897,10 +897,13 @@ hipError_t launch_tiles(const W4A4Args& a, hipStream_t stream) {
 }
 
 // Tile choice: 256x256 when that gives at least one tile per CU of the
-// chip, else 128x128.  0: 256x256, 1: 128x256, 2: 128x128.
+// chip, else 128x256 when that does (fewer decodes per MFMA than 128x128:
+// 8192x1024x4096 took 63-64 against 68-70 us), else 128x128.  0: 256x256,
+// 1: 128x256, 2: 128x128.
 int tile_choice(int64_t M, int64_t N) {
   const int64_t t0 = ((M + 255) / 256) * ((N + 255) / 256);
-  return t0 >= 256 ? 0 : 2;
+  const int64_t t1 = ((M + 127) / 128) * ((N + 255) / 256);
+  return t0 >= 256 ? 0 : (t1 >= 256 ? 1 : 2);
 }
 
 template <bool kFused, bool kSilu = false>
