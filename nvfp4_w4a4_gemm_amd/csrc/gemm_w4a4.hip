@@ -103,6 +103,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
+// A float at a wave-uniform address, by a scalar load (the constant address
+// space: the value is not written while the kernel runs).
+__device__ __forceinline__ float load_uniform(const float* ptr) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) float*>(
+      reinterpret_cast<uintptr_t>(ptr));
+}
+
 struct TileCoord {
   int64_t m0, m_end;      // rows [m0, min(m0 + BM, m_end)) of this tile
   int64_t n0;
@@ -223,7 +230,9 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   auto a_src_row = [&](int r) __attribute__((always_inline)) {
     int64_t g = tl.m0 + r;
     g = g < tl.m_end ? g : tl.m_end - 1;       // past the tile: clamp (not stored)
-    if (!kFused && p.a_row_index) g = p.a_row_index[g];
+    // (the tile walk runs without a row gather: no index load, whose wait
+    // would drain the DMA in flight, in its loop)
+    if (!kFused && !kPersist && p.a_row_index) g = p.a_row_index[g];
     return g;
   };
   auto b_src_row = [&](int r) __attribute__((always_inline)) {
@@ -642,7 +651,11 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
   uint8_t* const band_base = kPersist ? lds + slot(nk - 1) * kStageBytes : lds;
   // alpha_a alpha_b 2^8 per fragment column (one alpha_b per B row when B
   // concatenates several tensors, else the group's)
+  // (alpha_a and a group's alpha_b are uniform: scalar loads, so that no
+  // vector-memory wait drains the next tile's loads in flight)
   float scale[TN];
+  const float alpha_a = load_uniform(p.alpha_a);
+  const float alpha_g = p.alpha_b_rows ? 0.0f : load_uniform(p.alpha_b + tc.group);
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     float ab;
@@ -650,9 +663,9 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
       const int64_t col = tc.n0 + wn + 32 * j + fr_e;
       ab = p.alpha_b_rows[col < p.N ? col : p.N - 1];
     } else {
-      ab = p.alpha_b[tc.group];
+      ab = alpha_g;
     }
-    scale[j] = (*p.alpha_a) * ab * 256.0f;
+    scale[j] = alpha_a * ab * 256.0f;
   }
   const int64_t row_lim = tc.m0 + BM < tc.m_end ? tc.m0 + BM : tc.m_end;
   const bool want32 = p.y_f32 != nullptr, want16 = p.y_bf16 != nullptr;
@@ -811,9 +824,16 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
       silu_epilogue(std::false_type{});
     uint32_t hmax = max((uint32_t)hm2[0], (uint32_t)hm2[1]);
     hmax = wave_max_u32(hmax);
-    __shared__ uint32_t hred[4];
+    // the four wave maxima meet in the ring, past the H bands (one LDS
+    // array in the kernel: a second would make every fragment read of the
+    // main loop wait for all DMA in flight); LDS visibility needs only
+    // lgkmcnt(0) and the barrier, not the output stores
+    static_assert(4 * kBandRows * kPitchH + 16 <= (kPersist ? 1 : kRing) * kStageBytes,
+                  "wave maxima fit past the bands");
+    uint32_t* hred = reinterpret_cast<uint32_t*>(band_base + 4 * kBandRows * kPitchH);
     if (lane_e == 0) hred[wave] = hmax;
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(63));   // lgkmcnt(0) only
+    __builtin_amdgcn_s_barrier();
     if (tid == 0)
       p.h_partials[tile] =
           max(max(hred[0], hred[1]), max(hred[2], hred[3]));
