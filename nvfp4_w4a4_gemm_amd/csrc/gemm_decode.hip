@@ -285,8 +285,13 @@ constexpr int kMaxTiles = 8;
 // the ring carries the weight alone (half the LDS a stage, so more
 // workgroups fit on a CU).  20 KB takes up to 8 token rows at K = 4096
 // (24576 x 4096 at 8 tokens: 16.4 us against 18.9 staged); 16 rows there
-// (37 KB) ran no faster resident, and 6144 x 4096 slower.
+// (37 KB) ran no faster resident, and 6144 x 4096 slower.  With one stage
+// group a workgroup (more than two column tiles a CU) up to 48 KB stays
+// resident (51200 x 5120 at 8 tokens: 34.1 against 39.5 us, at 16 tokens
+// 38.4 against 40.4 us); with two or four groups the larger activation
+// lowers occupancy (7168 x 5120 at 16 tokens: 9.7 against 8.9 us).
 constexpr int kAResMaxBytes = 20 * 1024;
+constexpr int kAResWideMaxBytes = 48 * 1024;
 
 __host__ __device__ constexpr int decode_stage_bytes(int MT, bool ares) {
   return (ares ? 1 : 1 + MT) * kTileBytes + 256;
@@ -888,7 +893,10 @@ hipError_t launch_mt(const DecodeArgs& p, hipStream_t stream) {
     const int n_stages = (int)((p.K / 2 + kStageCodes - 1) / kStageCodes);
     if constexpr (MT == 1) {
       const int64_t ares_bytes = (p.M * n_stages + 7) / 8 * 8 * (int64_t)(kStageCodes + kStageScales);
-      if (ares_bytes <= kAResMaxBytes) return launch_one_mtile<true>(p, n_stages, stream);
+      const int64_t tiles = (p.N + kCols - 1) / kCols;
+      if (ares_bytes <= kAResMaxBytes ||
+          (ares_bytes <= kAResWideMaxBytes && tiles > 2 * (int64_t)device_cus()))
+        return launch_one_mtile<true>(p, n_stages, stream);
       return launch_one_mtile<false>(p, n_stages, stream);
     } else {
       return launch_lds<MT, kS, false, 1>(p, kS * decode_stage_bytes(MT, false), stream);

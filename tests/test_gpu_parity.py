@@ -262,7 +262,8 @@ def test_w4a4_gemm_deterministic():
                                    (1, 6000, 1536), (12, 5000, 4096), (16, 9000, 512),
                                    (14, 8400, 3072), (1, 20000, 512),
                                    (8, 300, 4096), (8, 6144, 4096), (8, 24576, 4096),
-                                   (7, 300, 4608)])
+                                   (7, 300, 4608), (16, 24576, 4096), (13, 9000, 4928),
+                                   (16, 9000, 5120)])
 def test_w4a4_gemm_decode_matches_oracle(m, n, k):
     """Decode shape (M <= 64): one, two and four 16-row tiles, K with a
     half chunk at the end (K % 32 == 16), a single column, ragged N; the
@@ -271,7 +272,9 @@ def test_w4a4_gemm_decode_matches_oracle(m, n, k):
     column tiles, two up to 512, else one (on 256 CUs): each with the
     activation resident and staged, with padding stages (K = 1536, 2560:
     3 and 5 stages of 512), and more column tiles than workgroups (20000
-    columns)."""
+    columns); with one stage group the activation resident up to 48 KB
+    (16 x 4096: 37 KB, 13 x 4928 with a partial last stage, 16 x 5120:
+    46 KB)."""
     xb, wb = quantized_pair(m, n, k, seed=3 * m + n + k)
     qa = nv.nvfp4_quantize_act(dev_bf16(xb))
     qw = nv.nvfp4_quantize_weights(dev_bf16(wb))
