@@ -30,7 +30,8 @@
 // reads 32 code bytes (two 16-byte chunks) and 4 scale bytes per fragment and
 // stage.  A and B use the same K order, which is all the contraction needs.
 // LDS rows are not padded; the 16-byte chunk c of row r sits at position
-// c ^ ((r >> 1) & 3) so that eight consecutive rows read conflict-free.
+// c ^ ((r >> 2) & 3), so that the 16 rows a ds_read_b128 serves at a time
+// (16 lanes) cover all 64 banks once.
 #include "device_common.h"
 #include "kernels.h"
 #include "quant_block.h"
