@@ -827,14 +827,16 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(W4A4Args p) {
     hmax = wave_max_u32(hmax);
     // the four wave maxima meet in the ring, past the H bands (one LDS
     // array in the kernel: a second would make every fragment read of the
-    // main loop wait for all DMA in flight); LDS visibility needs only
-    // lgkmcnt(0) and the barrier, not the output stores
+    // main loop wait for all DMA in flight); LDS-scoped workgroup fences
+    // order the exchange (lgkmcnt(0) and the barrier) without waiting for
+    // the output stores
     static_assert(4 * kBandRows * kPitchH + 16 <= (kPersist ? 1 : kRing) * kStageBytes,
                   "wave maxima fit past the bands");
     uint32_t* hred = reinterpret_cast<uint32_t*>(band_base + 4 * kBandRows * kPitchH);
     if (lane_e == 0) hred[wave] = hmax;
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(63));   // lgkmcnt(0) only
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     if (tid == 0)
       p.h_partials[tile] =
           max(max(hred[0], hred[1]), max(hred[2], hred[3]));
