@@ -433,6 +433,14 @@ def main():
         log("timing the layer with its producers (RMSNorm, SiLU*up) on both sides")
         result["layer_with_producers"] = producers_block(nv, torch, dev, x_dev, w_dev, wq,
                                                          qbuf, workspace, args)
+        # the other layer configurations, so that every configuration has a
+        # figure from this run: each GEMM beside hipBLASLt, each quantiser
+        log("timing configurations 1, 2, 3 and 5: each GEMM beside hipBLASLt, each quantiser")
+        result["other_configs"] = {}
+        for cfg in (1, 2, 3, 5):
+            result["other_configs"][str(cfg)] = sweep_config(cfg, nv, torch, dev, workspace,
+                                                              5, 2, bf16_kernel=False)
+            torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows, args.cpu_cols, m)
@@ -720,28 +728,37 @@ def decode_block(nv, torch, dev, workspace, steps, warmup):
 
 
 def sweep(args):
-    """Every GEMM and activation quantiser of configurations 1-5 on one GPU.
-
-    Per GEMM: the W4A4 kernel (BF16 out), the BF16 comparison kernel and
-    torch.matmul (hipBLASLt) on the same shapes; per activation tensor: the
-    whole quantiser (amax, alpha, tables, quantize).  Before each timing the
-    GPU runs 0.15 s of BF16 matmuls, so that the timings start from loaded
-    steady-state clocks, not from the idle left by host-side input
-    generation.  Inputs rotate over
-    copies totalling at least 512 MB where a tensor is smaller, so reads come
-    from HBM.  Configuration 4 also times the quantise-on-load GEMM;
-    configuration 5 the grouped GEMMs (hipBLASLt as one matmul per expert).
-    """
-    import numpy as np
+    """Every GEMM and activation quantiser of configurations 1-5 on one GPU,
+    one JSON line per configuration (sweep_config)."""
     import torch
 
     from nvfp4_w4a4_gemm_amd import binding as nv
-    from nvfp4_w4a4_gemm_amd.workloads import workload
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     ws = nv.new_workspace(dev)
     reps, warm = max(5, args.steps // 2), max(2, args.warmup)
+    for cfg in [int(c) for c in args.configs.split(",")]:
+        print(json.dumps(sweep_config(cfg, nv, torch, dev, ws, reps, warm)), flush=True)
+        torch.cuda.empty_cache()
+
+
+def sweep_config(cfg, nv, torch, dev, ws, reps, warm, bf16_kernel=True):
+    """Every GEMM and activation quantiser of one layer configuration.
+
+    Per GEMM: the W4A4 kernel (BF16 out), the BF16 comparison kernel (unless
+    bf16_kernel is false) and torch.matmul (hipBLASLt) on the same shapes;
+    per activation tensor: the whole quantiser (amax, alpha, tables,
+    quantize).  Before each timing the GPU runs 0.15 s of BF16 matmuls, so
+    that the timings start from loaded steady-state clocks, not from the idle
+    left by host-side input generation.  Inputs rotate over copies totalling
+    at least 512 MB where a tensor is smaller, so reads come from HBM.
+    Configuration 4 also times the quantise-on-load GEMM; configuration 5
+    the grouped GEMMs (hipBLASLt as one matmul per expert).
+    """
+    import numpy as np
+
+    from nvfp4_w4a4_gemm_amd.workloads import workload
 
     def copies(bits):
         n = max(1, min(8, -(-(512 << 20) // bits.nbytes)))
@@ -758,70 +775,71 @@ def sweep(args):
             torch.cuda.synchronize()
         del a
 
-    for cfg in [int(c) for c in args.configs.split(",")]:
-        wl = workload(cfg)
-        log(f"sweep: configuration {cfg}: {wl.title}")
-        out = {"config": cfg, "workload": wl.title, "gemms": [], "quantize": []}
-        if cfg == 5:
-            out.update(sweep_grouped(wl, nv, torch, dev, ws, copies, reps, warm, settle))
-            print(json.dumps(out), flush=True)
+    wl = workload(cfg)
+    log(f"sweep: configuration {cfg}: {wl.title}")
+    out = {"config": cfg, "workload": wl.title, "gemms": [], "quantize": []}
+    if cfg == 5:
+        out.update(sweep_grouped(wl, nv, torch, dev, ws, copies, reps, warm, settle, bf16_kernel))
+        return out
+    acts, qacts = {}, {}
+    for g in wl.gemms:
+        if g.act in acts:
             continue
-        acts, qacts = {}, {}
-        for g in wl.gemms:
-            if g.act in acts:
-                continue
-            xs = copies(wl.tensors[g.act].full())
-            acts[g.act] = xs
-            q = nv.nvfp4_quantize_act(xs[0], workspace=ws)
-            qacts[g.act] = q
-            settle()
-            t = time_ms(torch, lambda i: nv.nvfp4_quantize_act(xs[i % len(xs)], out=q,
-                                                               workspace=ws), reps, warm)
-            el = xs[0].numel()
-            gbps = el * (QUANT_BYTES_PER_ELEM + AMAX_BYTES_PER_ELEM) / (t * 1e-3) / 1e9
-            out["quantize"].append({"tensor": g.act, "shape": list(xs[0].shape),
-                                    "ms": round(t, 4), "gbps": round(gbps, 1),
-                                    "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)})
-        layer = {"w4a4_ms": sum(q["ms"] for q in out["quantize"]), "bf16_ms": 0.0,
-                 "hipblaslt_ms": 0.0}
-        for g in wl.gemms:
-            w = nv.to_device_bf16(wl.tensors[g.weight].full(), dev)
-            qw = nv.nvfp4_quantize_weights(w, workspace=ws)
-            xs, qa = acts[g.act], qacts[g.act]
-            mm, kk, nn = xs[0].shape[0], xs[0].shape[1], w.shape[0]
-            y = torch.empty(mm, nn, dtype=torch.bfloat16, device=dev)
-            fl = 2.0 * mm * nn * kk
-            settle()
-            t4 = time_ms(torch, lambda i: nv.w4a4_gemm(qa, qw, f32=False, y_bf16=y), reps, warm)
+        xs = copies(wl.tensors[g.act].full())
+        acts[g.act] = xs
+        q = nv.nvfp4_quantize_act(xs[0], workspace=ws)
+        qacts[g.act] = q
+        settle()
+        t = time_ms(torch, lambda i: nv.nvfp4_quantize_act(xs[i % len(xs)], out=q,
+                                                           workspace=ws), reps, warm)
+        el = xs[0].numel()
+        gbps = el * (QUANT_BYTES_PER_ELEM + AMAX_BYTES_PER_ELEM) / (t * 1e-3) / 1e9
+        out["quantize"].append({"tensor": g.act, "shape": list(xs[0].shape),
+                                "ms": round(t, 4), "gbps": round(gbps, 1),
+                                "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)})
+    layer = {"w4a4_ms": sum(q["ms"] for q in out["quantize"]), "hipblaslt_ms": 0.0}
+    if bf16_kernel:
+        layer["bf16_ms"] = 0.0
+    for g in wl.gemms:
+        w = nv.to_device_bf16(wl.tensors[g.weight].full(), dev)
+        qw = nv.nvfp4_quantize_weights(w, workspace=ws)
+        xs, qa = acts[g.act], qacts[g.act]
+        mm, kk, nn = xs[0].shape[0], xs[0].shape[1], w.shape[0]
+        y = torch.empty(mm, nn, dtype=torch.bfloat16, device=dev)
+        fl = 2.0 * mm * nn * kk
+        settle()
+        t4 = time_ms(torch, lambda i: nv.w4a4_gemm(qa, qw, f32=False, y_bf16=y), reps, warm)
+        th = time_ms(torch, lambda i: torch.matmul(xs[i % len(xs)], w.t()), reps, warm)
+        rec = {"gemm": g.name, "m": mm, "n": nn, "k": kk, "w4a4_ms": round(t4, 4),
+               "tflops": round(fl / (t4 * 1e-3) / 1e12, 1),
+               "frac_of_f16_mfma_peak": round(fl / (t4 * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+               "hipblaslt_ms": round(th, 4), "speedup_vs_hipblaslt": round(th / t4, 3)}
+        if bf16_kernel:
             tb = time_ms(torch, lambda i: nv.bf16_gemm_baseline(xs[i % len(xs)], w, f32=False),
                          reps, warm)
-            th = time_ms(torch, lambda i: torch.matmul(xs[i % len(xs)], w.t()), reps, warm)
-            rec = {"gemm": g.name, "m": mm, "n": nn, "k": kk, "w4a4_ms": round(t4, 4),
-                   "tflops": round(fl / (t4 * 1e-3) / 1e12, 1),
-                   "frac_of_f16_mfma_peak": round(fl / (t4 * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-                   "bf16_ms": round(tb, 4), "hipblaslt_ms": round(th, 4),
-                   "speedup_vs_bf16": round(tb / t4, 3), "speedup_vs_hipblaslt": round(th / t4, 3)}
-            if cfg == 4:
-                tf = time_ms(torch, lambda i: nv.w4a4_gemm_fused_act(
-                    xs[i % len(xs)], qa.alpha, qw, f32=False, y_bf16=y, workspace=ws), reps, warm)
-                rec["fused_quantize_gemm_ms"] = round(tf, 4)
-            out["gemms"].append(rec)
-            layer["w4a4_ms"] += t4
+            rec["bf16_ms"] = round(tb, 4)
+            rec["speedup_vs_bf16"] = round(tb / t4, 3)
             layer["bf16_ms"] += tb
-            layer["hipblaslt_ms"] += th
-            log(f"  {g.name} {mm}x{nn}x{kk}: w4a4 {t4:.3f} ms ({rec['tflops']} TFLOP/s), "
-                f"bf16 {tb:.3f} ms, hipBLASLt {th:.3f} ms")
-            del w, qw, y
-            torch.cuda.empty_cache()
-        layer["speedup_vs_bf16"] = round(layer["bf16_ms"] / layer["w4a4_ms"], 3)
-        layer["speedup_vs_hipblaslt"] = round(layer["hipblaslt_ms"] / layer["w4a4_ms"], 3)
-        out["layer"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in layer.items()}
-        print(json.dumps(out), flush=True)
-        del acts, qacts
+        if cfg == 4 and bf16_kernel:
+            tf = time_ms(torch, lambda i: nv.w4a4_gemm_fused_act(
+                xs[i % len(xs)], qa.alpha, qw, f32=False, y_bf16=y, workspace=ws), reps, warm)
+            rec["fused_quantize_gemm_ms"] = round(tf, 4)
+        out["gemms"].append(rec)
+        layer["w4a4_ms"] += t4
+        layer["hipblaslt_ms"] += th
+        log(f"  {g.name} {mm}x{nn}x{kk}: w4a4 {t4:.3f} ms ({rec['tflops']} TFLOP/s), "
+            f"hipBLASLt {th:.3f} ms")
+        del w, qw, y
         torch.cuda.empty_cache()
+    if bf16_kernel:
+        layer["speedup_vs_bf16"] = round(layer["bf16_ms"] / layer["w4a4_ms"], 3)
+    layer["speedup_vs_hipblaslt"] = round(layer["hipblaslt_ms"] / layer["w4a4_ms"], 3)
+    out["layer"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in layer.items()}
+    del acts, qacts
+    return out
 
 
-def sweep_grouped(wl, nv, torch, dev, ws, copies, reps, warm, settle):
+def sweep_grouped(wl, nv, torch, dev, ws, copies, reps, warm, settle, bf16_kernel=True):
     """Configuration 5: quantise X once, gather by routing, grouped GEMMs."""
     token_of_row, offsets = wl.routing()
     off_t = torch.from_numpy(offsets).to(dev)
@@ -829,7 +847,9 @@ def sweep_grouped(wl, nv, torch, dev, ws, copies, reps, warm, settle):
     res = {"gemms": [], "quantize": []}
     xs = copies(wl.tensors["X"].full())
     hs = copies(wl.tensors["H"].full())
-    layer = {"w4a4_ms": 0.0, "bf16_ms": 0.0, "hipblaslt_ms": 0.0}
+    layer = {"w4a4_ms": 0.0, "hipblaslt_ms": 0.0}
+    if bf16_kernel:
+        layer["bf16_ms"] = 0.0
     for name, act, wname, gather in (("gate_up_proj", xs, "W_gu", tok_t),
                                      ("down_proj", hs, "W_down", None)):
         q = nv.nvfp4_quantize_act(act[0], workspace=ws)
@@ -858,30 +878,34 @@ def sweep_grouped(wl, nv, torch, dev, ws, copies, reps, warm, settle):
                                                            a_row_index=gather, f32=False,
                                                            y_bf16=y), reps, warm)
         xg = act[0].index_select(0, tok_t.long()) if gather is not None else act[0]
-        tb = time_ms(torch, lambda i: nv.bf16_gemm_baseline(xg, w, group_offsets=off_t,
-                                                            f32=False), reps, warm)
+        tb = (time_ms(torch, lambda i: nv.bf16_gemm_baseline(xg, w, group_offsets=off_t,
+                                                             f32=False), reps, warm)
+              if bf16_kernel else None)
         bounds = offsets.tolist()
 
         def blas(i):
             for e in range(wl.experts):
                 torch.matmul(xg[bounds[e]:bounds[e + 1]], w[e].t())
         th = time_ms(torch, blas, max(3, reps // 2), 1)
-        res["gemms"].append({"gemm": name, "m": mm, "n": nn, "k": kk, "groups": wl.experts,
-                             "w4a4_ms": round(t4, 4),
-                             "tflops": round(fl / (t4 * 1e-3) / 1e12, 1),
-                             "frac_of_f16_mfma_peak": round(fl / (t4 * 1e-3) / 1e12 /
-                                                            MFMA_F16_PEAK_TFLOPS, 4),
-                             "bf16_ms": round(tb, 4), "hipblaslt_per_expert_ms": round(th, 4),
-                             "speedup_vs_bf16": round(tb / t4, 3),
-                             "speedup_vs_hipblaslt": round(th / t4, 3)})
+        rec = {"gemm": name, "m": mm, "n": nn, "k": kk, "groups": wl.experts,
+               "w4a4_ms": round(t4, 4),
+               "tflops": round(fl / (t4 * 1e-3) / 1e12, 1),
+               "frac_of_f16_mfma_peak": round(fl / (t4 * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+               "hipblaslt_per_expert_ms": round(th, 4),
+               "speedup_vs_hipblaslt": round(th / t4, 3)}
+        if bf16_kernel:
+            rec["bf16_ms"] = round(tb, 4)
+            rec["speedup_vs_bf16"] = round(tb / t4, 3)
+            layer["bf16_ms"] += tb
+        res["gemms"].append(rec)
         layer["w4a4_ms"] += t4
-        layer["bf16_ms"] += tb
         layer["hipblaslt_ms"] += th
-        log(f"  {name} grouped {mm}x{nn}x{kk}: w4a4 {t4:.3f} ms, bf16 {tb:.3f} ms, "
+        log(f"  {name} grouped {mm}x{nn}x{kk}: w4a4 {t4:.3f} ms, "
             f"hipBLASLt per expert {th:.3f} ms")
         del w, qws, b_codes, b_scales, y, xg
         torch.cuda.empty_cache()
-    layer["speedup_vs_bf16"] = round(layer["bf16_ms"] / layer["w4a4_ms"], 3)
+    if bf16_kernel:
+        layer["speedup_vs_bf16"] = round(layer["bf16_ms"] / layer["w4a4_ms"], 3)
     layer["speedup_vs_hipblaslt"] = round(layer["hipblaslt_ms"] / layer["w4a4_ms"], 3)
     res["layer"] = {k: round(v, 4) for k, v in layer.items()}
     return res
