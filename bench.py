@@ -438,8 +438,13 @@ def main():
         log("timing configurations 1, 2, 3 and 5: each GEMM beside hipBLASLt, each quantiser")
         result["other_configs"] = {}
         for cfg in (1, 2, 3, 5):
-            result["other_configs"][str(cfg)] = sweep_config(cfg, nv, torch, dev, workspace,
-                                                              5, 2, bf16_kernel=False)
+            try:
+                result["other_configs"][str(cfg)] = sweep_config(cfg, nv, torch, dev, workspace,
+                                                                  5, 2, bf16_kernel=False)
+            except Exception as exc:      # the headline line is printed regardless
+                torch.cuda.synchronize()
+                result["other_configs"][str(cfg)] = {"error": f"{type(exc).__name__}: {exc}"}
+                log(f"configuration {cfg} not timed: {exc}")
             torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
