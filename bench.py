@@ -419,7 +419,27 @@ def main():
     }
 
     if not args.no_extras:
-        del outs
+        # the same steps replayed from HIP graphs (two steps a graph, every
+        # replay checked against the eager result): no host launch cost or
+        # launch gaps between the 16 W4A4 launches or the 4 hipBLASLt ones
+        log("timing the layer step replayed from HIP graphs, W4A4 and hipBLASLt")
+        bl_out = {name: torch.empty(m, w_dev[wname].shape[0], dtype=torch.bfloat16, device=dev)
+                  for _, wname, name in LAYER}
+
+        def blas_step_out(i):
+            for xname, wname, name in LAYER:
+                torch.matmul(x_dev[xname], w_dev[wname].t(), out=bl_out[name])
+        reps_g = max(5, args.steps // 2)
+        settle_with(torch, w4a4_step, args.settle_ms)
+        g_w4 = graph_ms(torch, w4a4_step, 2, reps_g, check=lambda: outs["down"])
+        settle_with(torch, blas_step_out, args.settle_ms)
+        g_bl = graph_ms(torch, blas_step_out, 2, reps_g, check=lambda: bl_out["down"])
+        result["graph_step"] = {"w4a4_ms_per_step": round(g_w4, 4),
+                                "hipblaslt_ms_per_step": round(g_bl, 4),
+                                "speedup_vs_hipblaslt": round(g_bl / g_w4, 3),
+                                "steps_per_graph": 2, "replays": reps_g}
+        log(f"graph-replayed step: W4A4 {g_w4:.3f} ms, hipBLASLt {g_bl:.3f} ms")
+        del outs, bl_out
         torch.cuda.empty_cache()
         result["attention_qwen3_8b_m8192"] = attention_block(nv, torch, dev, workspace, args)
         log("timing RMSNorm with the quantiser fused in, against RMSNorm then quantise")
